@@ -1,0 +1,177 @@
+"""Benchmark of one LongCat Sparse Attention layer forward on one MI355X.
+
+Workload (decode sweep): a batch of 32 single-token decode queries, bf16; Lightning Indexer with
+64 heads x 128 dims over the middle region, flat top-1024, 16 sink + 1024 window + 1024 sparse
+tokens, attention of 128 heads over the 576-dim MLA latent; 64 planted needles per sequence;
+inputs seeded and resident in HBM before timing starts.  A step is one full layer forward
+(lsa_layer_fwd: indexer scoring, top-K, hybrid attention) over the batch.  The headline value is
+the layer latency at KV length 1M; the 128K leg is reported beside it.
+
+Prints one JSON line.  Single GPU only.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12        # B/s, MI355X HBM3E
+BF16_PEAK = 2.5e15       # FLOP/s dense MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_on_stream(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e-3  # seconds per call
+
+
+def run_length(L, batch, steps, warmup, seed=0):
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    t0 = time.time()
+    x = synth.decode_sweep(L, device="cuda", seed=seed, batch=batch)
+    torch.cuda.synchronize()
+    log(f"[bench] L={L}: inputs ready in {time.time() - t0:.1f}s")
+    c = x["cfg"]
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"])
+    layer = lsa.Layer(c, rows, torch.bfloat16, "cuda")
+    n = batch
+    idx = torch.full((n, c["k_sparse"]), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, c["H"], c["Dv"]), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((n, c["H"]), dtype=torch.float32, device="cuda")
+
+    def step():
+        layer(x["q"], x["kv"], idx, out, lse, q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+
+    # Whole-step timing: K steps between two synchronisations.
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t_start) / steps
+    t_step_ev = time_on_stream(step, steps, 0)
+    # The dominant kernel alone: the indexer scoring launch of the layer (same grid, same stream).
+    scores = torch.empty((n, L), dtype=torch.float32, device="cuda")
+    bud = (c["k_sink"], c["k_swa"], c["k_sparse"])
+    t_score = time_on_stream(lambda: lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], bud, scores=scores),
+                             steps, warmup)
+    # Needle sanity (not timed): every planted needle is selected.
+    got = idx.cpu().numpy()
+    recall = sum(len(set(p) & set(got[b].tolist())) for b, p in enumerate(x["needles"])) / max(
+        1, sum(len(p) for p in x["needles"]))
+    mid = L - c["k_sink"] - c["k_swa"]
+    k_bytes = n * mid * 128 * 2                       # indexer keys (the dominant stream)
+    attn_bytes = n * (c["k_sink"] + c["k_swa"] + c["k_sparse"]) * 576 * 2
+    io_bytes = n * (64 * 128 * 2 + 64 * 4 + 128 * 576 * 2 + 128 * 512 * 2 + 128 * 4 + c["k_sparse"] * 4)
+    alg_bytes = k_bytes + attn_bytes + io_bytes
+    flops = n * (mid * 64 * 128 * 2 + (c["k_sink"] + c["k_swa"] + c["k_sparse"]) * 128 * (576 + 512) * 2)
+    del scores
+    res = dict(L=L, batch=n, latency_us=t_step * 1e6, latency_us_events=t_step_ev * 1e6,
+               score_kernel_us=t_score * 1e6, score_kernel_bytes=k_bytes, alg_bytes=alg_bytes, flops=flops,
+               hbm_frac_layer=alg_bytes / t_step / HBM_PEAK, score_kernel_gbs=k_bytes / t_score / 1e9,
+               needle_recall=recall)
+    log(f"[bench] L={L}: layer {t_step * 1e6:.1f} us ({res['hbm_frac_layer'] * 100:.1f}% HBM), score kernel "
+        f"{t_score * 1e6:.1f} us = {res['score_kernel_gbs']:.0f} GB/s, needle recall {recall:.3f}")
+    del x, layer, idx, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(L=131072, rows=4, batch=32, seed=0):
+    """The oracle on a bounded sample: `rows` of the 32 rows of the L-token decode batch, one thread
+    per row; extrapolated to the whole batch at the same thread count."""
+    import numpy as np
+    import torch
+
+    import oracle as ref
+    import synth
+    x = synth.decode_batch([L] * rows, device="cuda", seed=seed)
+    h = synth.to_host
+    o = dict(kv_off=x["kv_off_host"].numpy(), row_seq=x["row_seq_host"].numpy(), row_pos=x["row_pos_host"].numpy(),
+             q_idx=h(x["q_idx"]), w=h(x["w"]), k_idx=h(x["k_idx"]), q=h(x["q"]), kv=h(x["kv"]))
+    del x
+    torch.cuda.empty_cache()
+    t0 = time.perf_counter()
+    ref.layer_fwd(dict(HI=64, dI=128, H=128, Dqk=576, Dv=512, scale=1 / math.sqrt(576), k_sink=16, k_swa=1024,
+                       k_sparse=1024, is_owner=1), o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"],
+                  o["k_idx"], o["q"], o["kv"], threads=rows)
+    dt = time.perf_counter() - t0
+    batch_us = dt * (batch / rows) * 1e6
+    log(f"[bench] oracle: {rows} rows at L={L} in {dt:.1f}s on {rows} threads")
+    return dict(value=batch_us, unit="us", cores=rows, kind="oracle",
+                sample=f"{rows} of the {batch} rows of the L={L} decode batch (one thread per row), "
+                       f"{dt:.2f} s wall, extrapolated x{batch // rows} to the whole {batch}-row batch at L={L}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--lengths", default="131072,1048576")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    lengths = [int(v) for v in args.lengths.split(",")]
+    legs = [run_length(L, args.batch, args.steps, args.warmup) for L in lengths]
+    head = legs[-1]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(batch=args.batch)
+    line = {
+        "metric": "LSA layer fwd latency (us) at 128K/1M decode; % HBM peak and % MFMA peak",
+        "value": round(head["latency_us"], 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["latency_us"] / 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"decode batch {args.batch} x 1 query, KV {head['L']}, bf16, HI=64 dI=128, "
+                               f"H=128 latent 576/512, K=16+1024+1024, flat indexer, 64 needles/seq",
+                   "global_batch": args.batch, "seq_len": head["L"], "parallelism": "single GPU"},
+        "legs": {str(r["L"]): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in legs},
+        "queries_per_s": round(args.batch / (head["latency_us"] * 1e-6), 1),
+        "hbm_frac_layer": round(head["hbm_frac_layer"], 4),
+        "mfma_frac_layer": round(head["flops"] / (head["latency_us"] * 1e-6) / BF16_PEAK, 4),
+        "roofline": {"kernel": "score_mfma_kernel (flat indexer scoring)", "bound": "hbm",
+                     "achieved": round(head["score_kernel_gbs"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(head["score_kernel_gbs"] * 1e9 / HBM_PEAK, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,505 @@
+// attn.hip -- hybrid sparse attention over the MLA latent KV on gfx950.
+//
+// For query row r at position t:  S = sink(t) u swa(t) u (indexer picks in mid(t))
+//   z_s = scale * q_h . kv_s[0:d_qk],  out_h = sum_s softmax(z)_s kv_s[0:d_v],  lse_h = log sum_s e^{z_s}
+// ([summary] "DSA Mechanism Formalization": attention over the selected latent rows; [paper] §4.1.1:
+// the contiguous sink+window part and the gathered part are processed separately and merged by
+// online-softmax rescaling).
+//
+// The selected set is enumerated as one list: j < n_sink -> s = j; then the window rows (one
+// contiguous run); then the compacted indexer picks.  The list is cut into 32-row tiles; the
+// contiguous part is read as whole 1,152-byte rows in address order, the gathered part as
+// independent rows, both through the same LDS tile.  A row's list can be split over several
+// blocks (flash-decoding style); each writes (m, l, unnormalised o) partials that a merge kernel
+// combines with the same rescaling rule.
+//
+// bf16 kernel, 576 / 512 latent: a block holds 128 heads (8 waves x 16 heads).  Per 32-row tile:
+//   S^T[32 rows x 16 heads] = K_tile . Q^T       36 x v_mfma_f32_16x16x32_bf16 (Q^T lives in VGPRs)
+//   online softmax per head                      a lane owns one head; two xor shuffles
+//   O^T[512 x 16 heads] += V^T_tile . P^T        32 x v_mfma_f32_16x16x32_bf16 (128 accumulators)
+// P^T comes straight out of the S^T accumulator layout as the B operand.  Each tile is staged
+// with coalesced 16-byte loads into a row-major K tile in LDS; V^T is then built from it in LDS
+// (with the row permutation that matches the accumulator layout) using 16-byte stores that touch
+// all 32 banks, so every MFMA operand is one 16-byte LDS read.  The next tile's rows are loaded
+// into registers while the current one is multiplied.
+#include "lsa_kernels.hpp"
+
+namespace lsa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kRowsPerTile = 32;
+constexpr int kHeadsPerWave = 16;
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = kAttnWaves * 64;
+constexpr int kHeadsPerBlock = kHeadsPerWave * kAttnWaves;
+constexpr int kMaxSparse = 4096;
+constexpr int kKStride = kDqk + 8;         // bf16 elements per LDS K row (1,168 B)
+constexpr int kVtStride = kRowsPerTile + 8; // bf16 elements per LDS V^T row (80 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplitMerge = 64;
+
+// ------------------------------------------------------------------ selected-set enumeration
+
+struct SelList {
+    int64_t base;      // first token row of the sequence
+    int n_sink;        // j in [0, n_sink): s = j
+    int64_t swa_lo;    // j in [n_sink, n_sink + n_swa): s = swa_lo + (j - n_sink)
+    int n_swa;
+    int n_sparse;      // j beyond: s = sparse[j - n_sink - n_swa]
+    int total;
+};
+
+// Compacts the usable indexer picks of a row into LDS (ascending input keeps its order):
+// an entry is used when it lies in mid(t) and differs from the entry before it.
+__device__ inline int compact_picks(const int32_t *pick_row, int k_sparse, const SiRanges &g, int32_t *sparse,
+                                    int32_t *scan_tmp)
+{
+    const int nt = blockDim.x;
+    const int tid = threadIdx.x;
+    const int per = (k_sparse + nt - 1) / nt;
+    const int i0 = tid * per;
+    int cnt = 0;
+    for (int i = i0; i < i0 + per && i < k_sparse; ++i) {
+        int32_t s = pick_row[i];
+        bool ok = s >= g.mid_lo && s < g.mid_hi && (i == 0 || pick_row[i - 1] != s);
+        cnt += ok ? 1 : 0;
+    }
+    scan_tmp[tid] = cnt;
+    __syncthreads();
+    // exclusive scan (nt <= 512, serial over waves is fine: done once per block)
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < nt; ++i) {
+            int c = scan_tmp[i];
+            scan_tmp[i] = acc;
+            acc += c;
+        }
+        scan_tmp[nt] = acc;
+    }
+    __syncthreads();
+    int o = scan_tmp[tid];
+    for (int i = i0; i < i0 + per && i < k_sparse; ++i) {
+        int32_t s = pick_row[i];
+        bool ok = s >= g.mid_lo && s < g.mid_hi && (i == 0 || pick_row[i - 1] != s);
+        if (ok)
+            sparse[o++] = s;
+    }
+    int total = scan_tmp[nt];
+    __syncthreads();
+    return total;
+}
+
+__device__ inline SelList make_sel(const RowInfo &ri, const SiRanges &g, int n_sparse)
+{
+    SelList L;
+    L.base = ri.base;
+    L.n_sink = (int)g.sink_hi;
+    L.swa_lo = g.swa_lo;
+    L.n_swa = (int)(g.swa_hi - g.swa_lo);
+    L.n_sparse = ri.valid ? n_sparse : 0;
+    L.total = ri.valid ? L.n_sink + L.n_swa + L.n_sparse : 0;
+    return L;
+}
+
+__device__ inline int64_t sel_pos(const SelList &L, const int32_t *sparse, int j)
+{
+    if (j < L.n_sink)
+        return j;
+    j -= L.n_sink;
+    if (j < L.n_swa)
+        return L.swa_lo + j;
+    return sparse[j - L.n_swa];
+}
+
+// ------------------------------------------------------------------ fp32 VALU kernel
+
+// One block per (row, head); logits in LDS; three passes (logits, max/sum, weighted sum of V).
+__global__ __launch_bounds__(256) void attn_valu_kernel(RowsDev rows, const float *__restrict__ q,
+                                                         const float *__restrict__ kv, int n_heads, int d_qk, int d_v,
+                                                         float scale, int k_sink, int k_swa, int k_sparse,
+                                                         const int32_t *__restrict__ idx, const int32_t *idx_row,
+                                                         float *__restrict__ out, float *__restrict__ lse)
+{
+    const int r = blockIdx.x, h = blockIdx.y;
+    __shared__ int32_t sparse[kMaxSparse];
+    __shared__ int32_t scan_tmp[257];
+    __shared__ float z[kMaxSparse + 2048 + 64];
+    __shared__ float qs[1024];
+    __shared__ float red[8];
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges g = si_ranges(ri, k_sink, k_swa);
+    const int ir = idx_row ? idx_row[r] : r;
+    const bool ir_ok = ir >= 0 && ir < rows.n_rows;  // an index row outside idx contributes no picks
+    int n_sp = compact_picks(idx + (int64_t)(ir_ok ? ir : 0) * k_sparse, ir_ok ? k_sparse : 0, g, sparse, scan_tmp);
+    const SelList L = make_sel(ri, g, n_sp);
+    const float *qh = q + ((int64_t)r * n_heads + h) * d_qk;
+    for (int d = threadIdx.x; d < d_qk; d += blockDim.x)
+        qs[d] = qh[d];
+    __syncthreads();
+    float *oh = out + ((int64_t)r * n_heads + h) * d_v;
+    if (L.total == 0) {
+        for (int d = threadIdx.x; d < d_v; d += blockDim.x)
+            oh[d] = 0.0f;
+        if (lse && threadIdx.x == 0)
+            lse[(int64_t)r * n_heads + h] = -INFINITY;
+        return;
+    }
+    const int wave = threadIdx.x >> 6, lane = lane_id();
+    for (int j = wave; j < L.total; j += blockDim.x / kWave) {
+        const float *kr = kv + (L.base + sel_pos(L, sparse, j)) * d_qk;
+        float acc = 0.0f;
+        for (int d = lane; d < d_qk; d += kWave)
+            acc = fmaf(qs[d], kr[d], acc);
+        acc = wave_sum(acc);
+        if (lane == 0)
+            z[j] = acc * scale;
+    }
+    __syncthreads();
+    float m = -INFINITY;
+    for (int j = threadIdx.x; j < L.total; j += blockDim.x)
+        m = fmaxf(m, z[j]);
+    m = wave_max(m);
+    if (lane == 0)
+        red[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float l = 0.0f;
+    for (int j = threadIdx.x; j < L.total; j += blockDim.x) {
+        float p = expf(z[j] - m);
+        z[j] = p;
+        l += p;
+    }
+    l = wave_sum(l);
+    if (lane == 0)
+        red[4 + wave] = l;
+    __syncthreads();
+    l = red[4] + red[5] + red[6] + red[7];
+    const float inv = 1.0f / l;
+    for (int d = threadIdx.x; d < d_v; d += blockDim.x) {
+        float acc = 0.0f;
+        for (int j = 0; j < L.total; ++j)
+            acc = fmaf(z[j], kv[(L.base + sel_pos(L, sparse, j)) * d_qk + d], acc);
+        oh[d] = acc * inv;
+    }
+    if (lse && threadIdx.x == 0)
+        lse[(int64_t)r * n_heads + h] = m + logf(l);
+}
+
+// ------------------------------------------------------------------ bf16 matrix-core kernel
+
+// V^T column order that makes the P^T accumulator rows line up with the MFMA K index: the S^T
+// accumulator of lane group g holds tile rows 4g + i and 16 + 4g + i (i < 4), which feed K
+// indices 8g + i and 8g + 4 + i.  So V^T column c = 8g + 4a + b holds tile row 16a + 4g + b.
+__device__ inline int vt_row(int c) { return 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3); }
+
+struct AttnPartial {
+    float *o;  // [n_rows][n_split][n_heads][kDv] unnormalised
+    float *m;  // [n_rows][n_split][n_heads] reference max (log2 domain, scale folded in)
+    float *l;  // [n_rows][n_split][n_heads]
+};
+
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows, const uint16_t *__restrict__ q,
+                                                                     const uint16_t *__restrict__ kv, int n_heads,
+                                                                     float scale, int k_sink, int k_swa, int k_sparse,
+                                                                     const int32_t *__restrict__ idx,
+                                                                     const int32_t *idx_row, int n_split,
+                                                                     uint16_t *__restrict__ out,
+                                                                     float *__restrict__ lse, AttnPartial part)
+{
+    const int split = blockIdx.x, r = blockIdx.y;
+    const int h_block = blockIdx.z * kHeadsPerBlock;
+    __shared__ __attribute__((aligned(16))) uint16_t kt[kRowsPerTile * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[kDv * kVtStride];
+    __shared__ int32_t sparse[kMaxSparse];
+    __shared__ int32_t scan_tmp[kAttnThreads + 1];
+    __shared__ int64_t tile_pos[kRowsPerTile];
+
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges g = si_ranges(ri, k_sink, k_swa);
+    const int ir = idx_row ? idx_row[r] : r;
+    const bool ir_ok = ir >= 0 && ir < rows.n_rows;  // an index row outside idx contributes no picks
+    const int n_sp = compact_picks(idx + (int64_t)(ir_ok ? ir : 0) * k_sparse, ir_ok ? k_sparse : 0, g, sparse,
+                                   scan_tmp);
+    const SelList L = make_sel(ri, g, n_sp);
+
+    const int n_tiles = (L.total + kRowsPerTile - 1) / kRowsPerTile;
+    const int tiles_per_split = (n_tiles + n_split - 1) / n_split;
+    const int tile_lo = split * tiles_per_split;
+    int tile_hi = tile_lo + tiles_per_split;
+    if (tile_hi > n_tiles)
+        tile_hi = n_tiles;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = lane_id();
+    const int n = lane & 15;  // head within the wave (B / C column) and A row
+    const int gq = lane >> 4; // lane group 0..3
+    const int head = h_block + wave * kHeadsPerWave + n;
+    const bool head_ok = head < n_heads;
+
+    // Q^T B-operand fragments: head `head`, depth 144 gq + 8 ks .. +8 for ks < 18.
+    u32x4 qb[18];
+    {
+        const uint16_t *qh = q + ((int64_t)r * n_heads + (head_ok ? head : 0)) * kDqk + gq * 144;
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks)
+            qb[ks] = head_ok ? *reinterpret_cast<const u32x4 *>(qh + 8 * ks) : u32x4{0, 0, 0, 0};
+    }
+    f32x4 o[32];  // O^T[dv = 16 mt + 4 gq + i][head n]
+#pragma unroll
+    for (int mt = 0; mt < 32; ++mt)
+        o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // reference max, log2 domain
+    float l_run = 0.0f;       // this lane's rows only; the four lane groups are added at the end
+    const float zs = scale * kLog2e;
+
+    // Staging: 32 rows x 72 chunks of 16 B = 2304 chunks over 512 threads.
+    constexpr int kChunksPerRow = kDqk / 8;
+    constexpr int kChunks = kRowsPerTile * kChunksPerRow;
+    constexpr int kPerThread = (kChunks + kAttnThreads - 1) / kAttnThreads;
+    u32x4 stage[kPerThread];
+
+    auto tile_row_pos = [&](int tile, int row) -> int64_t {
+        int j = tile * kRowsPerTile + row;
+        return j < L.total ? sel_pos(L, sparse, j) : -1;
+    };
+    auto load_stage = [&](int tile) {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int ch = tid + kAttnThreads * i;
+            int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
+            int64_t s = ch < kChunks ? tile_row_pos(tile, row) : -1;
+            stage[i] = s >= 0 ? *reinterpret_cast<const u32x4 *>(kv + (L.base + s) * kDqk + col * 8)
+                              : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    if (tile_lo < tile_hi)
+        load_stage(tile_lo);
+
+    for (int tile = tile_lo; tile < tile_hi; ++tile) {
+        // Publish the staged tile (K rows as they are) ...
+        if (tid < kRowsPerTile)
+            tile_pos[tid] = tile_row_pos(tile, tid);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            int ch = tid + kAttnThreads * i;
+            if (ch < kChunks) {
+                int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
+                *reinterpret_cast<u32x4 *>(&kt[row * kKStride + col * 8]) = stage[i];
+            }
+        }
+        __syncthreads();
+        if (tile + 1 < tile_hi)
+            load_stage(tile + 1);
+        // ... and V^T from it: item (dv, block of 8 V^T columns) gathers 8 rows of one dv column
+        // (consecutive lanes read consecutive dv of one row) and stores them as one 16-byte run.
+#pragma unroll
+        for (int i = 0; i < (kDv * 4) / kAttnThreads; ++i) {
+            int item = tid + kAttnThreads * i;
+            int dv = item & (kDv - 1), blk = item / kDv;
+            uint32_t e[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x)
+                e[x] = kt[vt_row(8 * blk + x) * kKStride + dv];
+            u32x4 pk;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                pk[x] = e[2 * x] | (e[2 * x + 1] << 16);
+            *reinterpret_cast<u32x4 *>(&vt[dv * kVtStride + 8 * blk]) = pk;
+        }
+        __syncthreads();
+
+        // S^T = K_tile . Q^T; lane (n, gq) ends with rows 4gq + i (sa) and 16 + 4gq + i (sb) of head n.
+        f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            const uint16_t *ra = &kt[n * kKStride + gq * 144];
+            const uint16_t *rb = &kt[(16 + n) * kKStride + gq * 144];
+#pragma unroll
+            for (int ks = 0; ks < 18; ++ks) {
+                u32x4 a0 = *reinterpret_cast<const u32x4 *>(ra + 8 * ks);
+                u32x4 a1 = *reinterpret_cast<const u32x4 *>(rb + 8 * ks);
+                bf16x8 bq = __builtin_bit_cast(bf16x8, qb[ks]);
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0), bq, sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1), bq, sb, 0, 0, 0);
+                if ((ks & 1) == 1)
+                    __builtin_amdgcn_sched_barrier(0);  // keep only a few LDS fragments live
+            }
+        }
+        // Online softmax in the log2 domain.
+        float z[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            z[i] = tile_pos[4 * gq + i] >= 0 ? sa[i] * zs : -INFINITY;
+            z[4 + i] = tile_pos[16 + 4 * gq + i] >= 0 ? sb[i] * zs : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            tmax = fmaxf(tmax, z[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        // Move the reference max only when it grows by more than 8 (a factor 256): the softmax is
+        // unchanged by the choice of reference, so O^T is rescaled only on those rare steps.
+        if (tmax > m_run + 8.0f) {
+            float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - tmax);
+            m_run = tmax;
+            l_run *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 32; ++mt)
+                o[mt] *= alpha;
+        }
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float pv = m_run == -INFINITY ? 0.0f : exp2f(z[i] - m_run);
+            l_run += pv;
+            pb[i] = (__bf16)pv;
+        }
+        // O^T += V^T . P^T  (one K step of 32 tile rows per 16-dv slice)
+        {
+            const uint16_t *vrow = &vt[n * kVtStride + 8 * gq];
+#pragma unroll
+            for (int mt = 0; mt < 32; ++mt) {
+                u32x4 a = *reinterpret_cast<const u32x4 *>(vrow + mt * 16 * kVtStride);
+                o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[mt], 0, 0, 0);
+                if ((mt & 3) == 3)
+                    __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+    }
+
+    float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    if (!head_ok)
+        return;
+    if (n_split == 1) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t *oh = out + ((int64_t)r * n_heads + head) * kDv;
+#pragma unroll
+        for (int mt = 0; mt < 32; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                oh[mt * 16 + 4 * gq + i] = float_to_bf16_bits(o[mt][i] * inv);
+        if (lse && gq == 0)
+            lse[(int64_t)r * n_heads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) / kLog2e : -INFINITY;
+    } else {
+        const int64_t slot = ((int64_t)r * n_split + split) * n_heads + head;
+        float *oh = part.o + slot * kDv;
+#pragma unroll
+        for (int mt = 0; mt < 32; ++mt)
+            *reinterpret_cast<f32x4 *>(&oh[mt * 16 + 4 * gq]) = o[mt];
+        if (gq == 0) {
+            part.m[slot] = m_run;
+            part.l[slot] = l_tot;
+        }
+    }
+}
+
+// Combines the split partials of one (row, head): the same rescaling rule as inside the kernel.
+__global__ __launch_bounds__(256) void attn_merge_kernel(int n_heads, int n_split, AttnPartial part,
+                                                          uint16_t *__restrict__ out, float *__restrict__ lse)
+{
+    const int r = blockIdx.x, h = blockIdx.y;
+    __shared__ float wsp[kMaxSplitMerge];
+    float mx = -INFINITY;
+    for (int s = 0; s < n_split; ++s)
+        mx = fmaxf(mx, part.m[((int64_t)r * n_split + s) * n_heads + h]);
+    float l = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+        int64_t slot = ((int64_t)r * n_split + s) * n_heads + h;
+        float ms = part.m[slot];
+        float wgt = ms == -INFINITY ? 0.0f : exp2f(ms - mx);
+        if (threadIdx.x == 0)
+            wsp[s] = wgt;
+        l += wgt * part.l[slot];
+    }
+    __syncthreads();
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t *oh = out + ((int64_t)r * n_heads + h) * kDv;
+    for (int d = threadIdx.x; d < kDv; d += blockDim.x) {
+        float acc = 0.0f;
+        for (int s = 0; s < n_split; ++s)
+            if (wsp[s] != 0.0f)
+                acc += wsp[s] * part.o[(((int64_t)r * n_split + s) * n_heads + h) * kDv + d];
+        oh[d] = float_to_bf16_bits(acc * inv);
+    }
+    if (lse && threadIdx.x == 0)
+        lse[(int64_t)r * n_heads + h] = l > 0.0f ? (mx + log2f(l)) / kLog2e : -INFINITY;
+}
+
+// ------------------------------------------------------------------ host
+
+constexpr int kMaxSplit = kMaxSplitMerge;
+
+static int pick_split(int n_rows, int n_heads, int k_total)
+{
+    int blocks_per_split = n_rows * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    int want = (256 + blocks_per_split - 1) / blocks_per_split;  // about one block per CU
+    int max_by_tiles = (k_total + kRowsPerTile - 1) / kRowsPerTile / 4;  // >= 4 tiles per split
+    if (want > max_by_tiles)
+        want = max_by_tiles;
+    if (want > kMaxSplit)
+        want = kMaxSplit;
+    return want < 1 ? 1 : want;
+}
+
+size_t attn_workspace_bytes(int dtype, int n_rows, int n_heads, int d_v, int k_total)
+{
+    if (dtype != 1)
+        return 0;
+    int ns = pick_split(n_rows, n_heads, k_total);
+    if (ns == 1)
+        return 0;
+    size_t slots = (size_t)n_rows * ns * n_heads;
+    return align_up(slots * kDv * sizeof(float)) + 2 * align_up(slots * sizeof(float));
+}
+
+bool attn_supported(int dtype, int n_heads, int d_qk, int d_v, int k_sparse, int k_total)
+{
+    if (k_sparse > kMaxSparse)
+        return false;
+    if (dtype == 1)
+        return n_heads % kHeadsPerWave == 0 && d_qk == kDqk && d_v == kDv;
+    return d_qk <= 1024 && d_v <= d_qk && k_total <= kMaxSparse + 2048 + 64;
+}
+
+hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, const void *kv, int n_heads, int d_qk,
+                              int d_v, float scale, int k_sink, int k_swa, int k_sparse, const int32_t *idx,
+                              const int32_t *idx_row, void *out, float *lse, void *ws, hipStream_t stream)
+{
+    if (rows.n_rows == 0)
+        return hipSuccess;
+    if (dtype != 1) {
+        hipLaunchKernelGGL(attn_valu_kernel, dim3(rows.n_rows, n_heads), dim3(256), 0, stream, rows, (const float *)q,
+                           (const float *)kv, n_heads, d_qk, d_v, scale, k_sink, k_swa, k_sparse, idx, idx_row,
+                           (float *)out, lse);
+        return hipGetLastError();
+    }
+    const int k_total = k_sink + k_swa + k_sparse;
+    const int ns = pick_split(rows.n_rows, n_heads, k_total);
+    AttnPartial part{nullptr, nullptr, nullptr};
+    if (ns > 1) {
+        size_t slots = (size_t)rows.n_rows * ns * n_heads;
+        char *p = (char *)ws;
+        part.o = (float *)p;
+        p += align_up(slots * kDv * sizeof(float));
+        part.m = (float *)p;
+        p += align_up(slots * sizeof(float));
+        part.l = (float *)p;
+    }
+    dim3 grid(ns, rows.n_rows, (n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kAttnThreads), 0, stream, rows, (const uint16_t *)q, (const uint16_t *)kv,
+                       n_heads, scale, k_sink, k_swa, k_sparse, idx, idx_row, ns, (uint16_t *)out, lse, part);
+    if (ns > 1)
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(rows.n_rows, n_heads), dim3(256), 0, stream, n_heads, ns, part,
+                           (uint16_t *)out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,56 @@
+// lsa_kernels.hpp -- host-side launchers of the liblsa kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lsa_dev.hpp"
+
+namespace lsa {
+
+// Row gating for the layer: when row_mode != nullptr, only rows with row_mode[r] == want run.
+struct RowGate {
+    const uint8_t *row_mode;
+    int want;
+};
+
+// --- indexer scoring (index_score.hip)
+enum ScoreMode { kScoreFlat = 0, kScorePaged = 1 };
+
+hipError_t launch_index_score(int dtype, const RowsDev &rows, int64_t max_kv_len, const void *q_idx, const float *w,
+                              const void *k_idx, int n_heads, int head_dim, int k_sink, int k_swa,
+                              const int32_t *pages, int M, int P, float *scores, int64_t ld, RowGate gate,
+                              hipStream_t stream);
+bool index_score_supported(int dtype, int n_heads, int head_dim);
+
+// HI stage 1: page scores (sums of sub-block scores per page), -inf for non-causal pages.
+hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len, const int64_t *sb_off,
+                              const void *q_idx, const float *w, const void *k_mean, int n_heads, int head_dim,
+                              int P, int B, float *page_scores, int64_t ld_ps, RowGate gate, hipStream_t stream);
+
+// --- sub-block means (hi.hip)
+hipError_t launch_page_means(int dtype, int n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
+                             int head_dim, int B, int64_t max_kv_len, int64_t first_token, void *k_mean,
+                             hipStream_t stream);
+
+// --- top-k (topk.hip)
+size_t topk_workspace_bytes(int n_rows, int k);
+hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages, int M,
+                       int P, int k, int32_t *idx, void *ws, RowGate gate, hipStream_t stream);
+
+// --- attention (attn.hip)
+size_t attn_workspace_bytes(int dtype, int n_rows, int n_heads, int d_v, int k_total);
+bool attn_supported(int dtype, int n_heads, int d_qk, int d_v, int k_sparse, int k_total);
+hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, const void *kv, int n_heads, int d_qk,
+                              int d_v, float scale, int k_sink, int k_swa, int k_sparse, const int32_t *idx,
+                              const int32_t *idx_row, void *out, float *lse, void *ws, hipStream_t stream);
+
+// --- layer helpers (layer.hip)
+hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
+                            uint8_t *row_mode, hipStream_t stream);
+
+// Rounds a byte count up to the workspace alignment.
+inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace lsa

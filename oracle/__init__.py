@@ -86,7 +86,7 @@ def _dt(a):
 
 
 def default_threads():
-    return max(1, os.cpu_count() or 1)
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 # ------------------------------------------------------------------------------------ scalars

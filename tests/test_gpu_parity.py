@@ -1,0 +1,419 @@
+"""GPU parity of every hot-path step against the CPU oracle, through the C ABI (small and ragged
+shapes that still span several tiles, plus the edge cases of the method)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_weighted_amd as lsa
+import oracle as ref
+import synth
+from parity_util import (assert_attn_close, assert_idx_sets_match, assert_scores_close, budget_of, f64, host,
+                         kth_best, log, near_tie, oracle_inputs, rows_of)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def custom_rows(lengths, rows, *, HI=64, dI=128, H=128, dtype=torch.bfloat16, seed=0, k_sink=16, k_swa=1024,
+                k_sparse=1024, attn=True):
+    """Sequences of the given lengths and explicit query rows (seq, t) with seeded Gaussian inputs."""
+    g = synth.generator(seed, DEV)
+    kv_off = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64)
+    tot = int(kv_off[-1])
+    n = len(rows)
+    row_seq = torch.tensor([r[0] for r in rows], dtype=torch.int32)
+    row_pos = torch.tensor([r[1] for r in rows], dtype=torch.int32)
+    x = dict(kv_off=kv_off.to(DEV), kv_off_host=kv_off, row_seq=row_seq.to(DEV), row_seq_host=row_seq,
+             row_pos=row_pos.to(DEV), row_pos_host=row_pos, max_len=max(lengths), lengths=list(lengths))
+    x["q_idx"] = synth.normal((n, HI, dI), 1 / math.sqrt(dI), g, DEV, dtype)
+    x["w"] = synth.softplus_normal((n, HI), g, DEV)
+    x["k_idx"] = synth.normal((max(tot, 1), dI), 1 / math.sqrt(dI), g, DEV, dtype)
+    if attn:
+        x["q"] = synth.normal((n, H, 576), 1.0, g, DEV, dtype)
+        x["kv"] = synth.normal((max(tot, 1), 576), 1.0, g, DEV, dtype)
+    x["cfg"] = dict(HI=HI, dI=dI, H=H, Dqk=576, Dv=512, scale=1 / math.sqrt(576), k_sink=k_sink, k_swa=k_swa,
+                    k_sparse=k_sparse, P=128, B=128, M=1024, hi_min_len=1 << 62, is_owner=1)
+    return x
+
+
+RAGGED_LENGTHS = [1, 17, 1041, 1042, 3001, 6000]
+RAGGED_ROWS = [(0, 0), (1, 16), (1, 5), (2, 1040), (2, 1039), (3, 1041), (3, 1000), (4, 3000), (4, 2048),
+               (5, 5999), (5, 4321), (5, 6000)]  # the last row is outside its sequence (t == L)
+
+
+# --------------------------------------------------------------------------------------------- a2 scores
+
+
+def test_index_score_fp32_tiny_prefill():
+    x = synth.tiny_prefill(device=DEV)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c))
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=2048)
+    log("fp32 scores worst err/tol", assert_scores_close(host(g), want))
+
+
+def test_index_score_bf16_ragged_and_edges():
+    x = custom_rows(RAGGED_LENGTHS, RAGGED_ROWS, attn=False)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    ld = x["max_len"] + 37
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), ld=ld)
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=ld)
+    log("bf16 scores worst err/tol", assert_scores_close(host(g), want))
+    assert np.all(np.isneginf(host(g)[-1]))  # a row outside its sequence scores nothing
+
+
+def test_index_score_bf16_page_mapped():
+    L = 9000
+    x = custom_rows([L, 4000], [(0, L - 1), (0, 5000), (1, 3999)], attn=False)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    P, M = 128, 12
+    pages = np.full((3, M), -1, np.int32)
+    pages[0, :10] = [0, 1, 7, 8, 30, 31, 55, 60, 69, 70]        # 70 is the partial last page of L = 9000
+    pages[1, :6] = [3, 9, 20, 30, 31, 39]                       # 31 straddles mid(5000) end; 39 beyond t
+    pages[2, :5] = [0, 5, 10, 23, 31]                            # 31 is beyond L = 4000
+    pg = torch.from_numpy(pages).to(DEV)
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), pages=pg, P=P, ld=M * P + 5)
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=M * P + 5, pages=pages, P=P)
+    log("paged scores worst err/tol", assert_scores_close(host(g), want))
+
+
+# --------------------------------------------------------------------------------------------- a7 top-K
+
+
+def _score_rows(rng, n_rows, n_cols, kind):
+    if kind == "gauss":
+        s = rng.standard_normal((n_rows, n_cols)).astype(np.float32)
+    elif kind == "ties":
+        s = rng.choice(np.array([-2.0, -0.0, 0.0, 0.5, 1.0, 3.0, np.inf], np.float32), (n_rows, n_cols))
+    elif kind == "equal":
+        s = np.full((n_rows, n_cols), 0.75, np.float32)
+    else:  # coarse quantised values: many ties at the threshold
+        s = (rng.integers(-50, 50, (n_rows, n_cols)) / 8.0).astype(np.float32)
+    s[rng.random((n_rows, n_cols)) < 0.1] = -np.inf
+    return s
+
+
+@pytest.mark.parametrize("n_rows,n_cols,K,kind", [
+    (3, 1, 1, "gauss"), (5, 100, 7, "gauss"), (4, 100, 200, "ties"), (4, 5000, 1024, "gauss"),
+    (4, 5000, 1024, "ties"), (3, 20000, 1024, "quant"), (2, 70000, 1024, "equal"), (1, 4096, 4096, "quant"),
+    (64, 3000, 112, "gauss"), (2, 300000, 1024, "quant")])
+def test_topk_bit_exact_on_oracle_style_scores(n_rows, n_cols, K, kind):
+    rng = np.random.default_rng(n_rows * 7919 + n_cols + K)
+    s = _score_rows(rng, n_rows, n_cols, kind)
+    s[0, : min(5, n_cols)] = -np.inf
+    want = ref.topk(s, K)
+    got = host(lsa.lsa_topk(torch.from_numpy(s).to(DEV), K))
+    assert np.array_equal(got, want), f"first differing row {np.argwhere((got != want).any(1))[:3].ravel()}"
+
+
+def test_topk_negative_zero_and_all_neg_inf_rows():
+    s = np.array([[0.0, -0.0, 0.0, -0.0, -1.0], [-np.inf] * 5, [-0.0, -np.inf, 0.0, -np.inf, -0.0]], np.float32)
+    got = host(lsa.lsa_topk(torch.from_numpy(s).to(DEV), 3))
+    assert np.array_equal(got, ref.topk(s, 3))
+    assert list(got[1]) == [-1, -1, -1]
+
+
+def test_topk_page_mapped_bit_exact():
+    rng = np.random.default_rng(5)
+    P, M = 128, 40
+    s = _score_rows(rng, 6, M * P, "quant")
+    pages = np.sort(rng.choice(5000, (6, M), replace=False), axis=1).astype(np.int32)
+    pages[:, -3:] = -1
+    s[:, -3 * P:] = -np.inf
+    s[2, 5 * P:6 * P] = 1.0   # a filled slot of a valid page with ties
+    want = ref.topk(s, 1024, pages=pages, P=P)
+    got = host(lsa.lsa_topk(torch.from_numpy(s).to(DEV), 1024, pages=torch.from_numpy(pages).to(DEV), P=P))
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------------------------- a3 means
+
+
+@pytest.mark.parametrize("dtype,B", [(torch.bfloat16, 128), (torch.bfloat16, 8), (torch.float32, 16)])
+def test_page_means_bit_exact(dtype, B):
+    lengths = [1, 127, 128, 129, 5000]
+    g = synth.generator(3, DEV)
+    kv_off = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64)
+    k = synth.normal((int(kv_off[-1]), 128), 1 / math.sqrt(128), g, DEV, dtype)
+    sb_off = lsa.sb_offsets(lengths, B)
+    got = lsa.lsa_page_means(kv_off.to(DEV), sb_off.to(DEV), k, B, max(lengths))
+    want = ref.page_means(kv_off.numpy(), sb_off.numpy(), host(k), B)
+    assert np.array_equal(host(got), want)
+    # incremental rebuild from token 4000 on: the rows it touches equal a full rebuild
+    k[kv_off[4] + 4000:] *= 2
+    got2 = lsa.lsa_page_means(kv_off.to(DEV), sb_off.to(DEV), k, B, max(lengths), k_mean=got.clone(),
+                              first_token=4000)
+    want2 = ref.page_means(kv_off.numpy(), sb_off.numpy(), host(k), B)
+    assert np.array_equal(host(got2), want2)
+
+
+# --------------------------------------------------------------------------------------------- a4/a5 HI
+
+
+@pytest.mark.parametrize("B", [128, 8])
+def test_page_recall_scores_and_pages(B):
+    lengths = [70000, 20000, 130]
+    rows = [(0, 69999), (1, 19999), (0, 40000), (2, 129)]
+    x = custom_rows(lengths, rows, attn=False, seed=11)
+    o = oracle_inputs(x)
+    P, M = 128, 64
+    sb_off = lsa.sb_offsets(lengths, B)
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], B)
+    km = synth.bits_to_bf16(km_o).to(DEV)             # both sides read the oracle's cache
+    ld = (max(lengths) + P - 1) // P
+    ps = torch.empty((len(rows), ld), dtype=torch.float32, device=DEV)
+    pages, _ = lsa.lsa_page_recall(rows_of(x), sb_off.to(DEV), x["q_idx"], x["w"], km, P, B, M, page_scores=ps)
+    want_ps = ref.page_scores(o["kv_off"], sb_off.numpy(), o["row_seq"], o["row_pos"], o["q_idx"], o["w"], km_o, P,
+                              B, ld)
+    log("page scores worst err/tol", assert_scores_close(host(ps), want_ps, "page scores"))
+    want_pages = ref.topk(want_ps, M)
+
+    assert_idx_sets_match(host(pages), want_pages, lambda r, d: near_tie(want_ps[r, d], kth_best(want_ps[r], M)),
+                          what="pages")
+    # fed the oracle's page scores, the selection is bit-exact
+    got = host(lsa.lsa_topk(torch.from_numpy(want_ps).to(DEV), M))
+    assert np.array_equal(got, want_pages)
+
+
+# --------------------------------------------------------------------------------------------- a8-a10 attention
+
+
+def _oracle_idx_for(x, k_sparse, rng):
+    """A valid ascending pick list per row drawn from mid(t) (what an indexer could return)."""
+    c = x["cfg"]
+    out = np.full((len(x["row_pos_host"]), k_sparse), -1, np.int32)
+    for r, (b, t) in enumerate(zip(x["row_seq_host"].tolist(), x["row_pos_host"].tolist())):
+        L = x["lengths"][b]
+        if t < 0 or t >= L:
+            continue
+        lo, hi = c["k_sink"], t - c["k_swa"] + 1
+        if hi > lo:
+            pick = np.sort(rng.choice(np.arange(lo, hi), min(k_sparse, hi - lo), replace=False))
+            out[r, :len(pick)] = pick
+    return out
+
+
+def test_attention_fp32_tiny_prefill_shape():
+    x = synth.tiny_prefill(device=DEV)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    rng = np.random.default_rng(1)
+    rows_sel = np.array([0, 1, 15, 16, 143, 144, 145, 300, 1023, 2047])
+    sub = {k: x[k][rows_sel] for k in ("q",)}
+    rs = torch.from_numpy(np.zeros(len(rows_sel), np.int32)).to(DEV)
+    rp = torch.from_numpy(rows_sel.astype(np.int32)).to(DEV)
+    rows = lsa.RowsDesc(x["kv_off"], rs, rp, 2048)
+    xs = dict(cfg=c, row_seq_host=torch.zeros(len(rows_sel), dtype=torch.int32),
+              row_pos_host=torch.from_numpy(rows_sel.astype(np.int32)), lengths=[2048])
+    idx = _oracle_idx_for(xs, c["k_sparse"], rng)
+    out, lse = lsa.lsa_hybrid_attn(rows, sub["q"], x["kv"], 512, c["scale"], budget_of(c),
+                                   torch.from_numpy(idx).to(DEV))
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], np.zeros(len(rows_sel)), rows_sel, o["q"][rows_sel], o["kv"], 512,
+                                     c["scale"], c["k_sink"], c["k_swa"], idx)
+    log("fp32 attn max err", assert_attn_close(host(out), want_o, host(lse), want_l, 1e-4))
+
+
+@pytest.mark.parametrize("budget", [(16, 1024, 1024), (16, 32, 64), (4, 100, 300)])
+def test_attention_bf16_vs_oracle(budget):
+    ks, kw, kp = budget
+    x = custom_rows(RAGGED_LENGTHS, RAGGED_ROWS, k_sink=ks, k_swa=kw, k_sparse=kp, seed=21)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    rng = np.random.default_rng(2)
+    idx = _oracle_idx_for(x, kp, rng)
+    idx[3, 1:4] = idx[3, 0]            # repeats are ignored
+    out, lse = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], budget,
+                                   torch.from_numpy(idx).to(DEV))
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], o["row_seq"], o["row_pos"], o["q"], o["kv"], 512, c["scale"], ks,
+                                     kw, idx)
+    log("bf16 attn max err", assert_attn_close(host(out), want_o, host(lse), want_l, 2e-2))
+    assert np.all(f64(host(out))[-1] == 0) and np.all(np.isneginf(host(lse)[-1]))
+
+
+def test_attention_bf16_many_rows_single_split():
+    # enough rows that each row runs in one block (no split partials)
+    lengths = [3000] * 4
+    rows = [(b, t) for b in range(4) for t in (1100, 2999, 2000, 1500)] * 20
+    x = custom_rows(lengths, rows, seed=5)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx = _oracle_idx_for(x, 1024, np.random.default_rng(3))
+    out, lse = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], budget_of(c),
+                                   torch.from_numpy(idx).to(DEV))
+    sel = np.arange(0, len(rows), 9)
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], o["row_seq"][sel], o["row_pos"][sel], o["q"][sel], o["kv"], 512,
+                                     c["scale"], 16, 1024, idx[sel])
+    assert_attn_close(host(out)[sel], want_o, host(lse)[sel], want_l, 2e-2)
+
+
+# --------------------------------------------------------------------------------------------- layer
+
+
+class OracleRanking:
+    """The oracle's own scores, to judge where GPU and oracle index sets may differ: a position is a
+    near-tie when its Eq. 1 score is within 1e-3 of the row's K-th best; under HI also when its page
+    score is within 1e-3 of the M-th best page score (the page ranking itself tied)."""
+
+    def __init__(self, o, c, sb_off=None, k_mean=None):
+        self.o, self.c = o, c
+        self.lengths = np.diff(o["kv_off"])
+        self.sb_off, self.k_mean = sb_off, k_mean
+        self.cache = {}
+
+    def _row(self, r):
+        if r not in self.cache:
+            o, c = self.o, self.c
+            sl = slice(r, r + 1)
+            flat = ref.index_score(o["kv_off"], o["row_seq"][sl], o["row_pos"][sl], o["q_idx"][sl], o["w"][sl],
+                                   o["k_idx"], c["k_sink"], c["k_swa"], ld=int(self.lengths.max()))[0]
+            b = int(o["row_seq"][r])
+            hi = self.k_mean is not None and self.lengths[b] >= c["hi_min_len"]
+            if not hi:
+                self.cache[r] = (flat, kth_best(flat, c["k_sparse"]), None, None)
+            else:
+                P, M = c["P"], c["M"]
+                ld = int((self.lengths.max() + P - 1) // P)
+                pages, ps = ref.page_recall(o["kv_off"], self.sb_off, o["row_seq"][sl], o["row_pos"][sl],
+                                            o["q_idx"][sl], o["w"][sl], self.k_mean, P, c["B"], M, ld=ld)
+                comp = ref.index_score(o["kv_off"], o["row_seq"][sl], o["row_pos"][sl], o["q_idx"][sl], o["w"][sl],
+                                       o["k_idx"], c["k_sink"], c["k_swa"], ld=M * P, pages=pages, P=P)[0]
+                self.cache[r] = (flat, kth_best(comp, c["k_sparse"]), ps[0], kth_best(ps[0], M))
+        return self.cache[r]
+
+    def accept(self, r, diff):
+        flat, theta, ps, theta_p = self._row(r)
+        ok = near_tie(flat[diff], theta)
+        if ps is not None:
+            ok |= near_tie(ps[diff // self.c["P"]], theta_p)
+        return ok
+
+
+def test_layer_tiny_prefill_fp32():
+    x = synth.tiny_prefill(device=DEV)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    w_idx, w_out, w_lse = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"],
+                                        o["q"], o["kv"])
+    _compare_layer(x, host(idx), host(out), host(lse), w_idx, w_out, w_lse, 1e-4, OracleRanking(o, c))
+    # needles: every planted key is picked by the row it was planted for
+    g_idx = host(idx)
+    for r, s in x["needles"]:
+        assert s in set(g_idx[r].tolist()), (r, s)
+
+
+def test_layer_bf16_decode_ragged():
+    lengths = [1040, 1041, 2000, 9000, 17000]
+    x = synth.decode_batch(lengths, device=DEV, seed=4, needles=8)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    w_idx, w_out, w_lse = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"],
+                                        o["q"], o["kv"])
+    _compare_layer(x, host(idx), host(out), host(lse), w_idx, w_out, w_lse, 2e-2, OracleRanking(o, c))
+    g_idx = host(idx)
+    for b, picks in enumerate(x["needles"]):
+        assert set(picks) <= set(g_idx[b].tolist())
+
+
+def test_layer_deterministic():
+    x = synth.decode_batch([5000, 12000], device=DEV, seed=6, needles=4)
+    c = x["cfg"]
+    a = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    b = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+
+
+def _hi_setup(lengths, M, B=128, seed=8, drafts=1, hi_min_len=0):
+    x = synth.decode_batch(lengths, device=DEV, seed=seed, needles=0, needle_pages=8, M=M, B=B, drafts=drafts,
+                           hi_min_len=hi_min_len)
+    sb_off = lsa.sb_offsets(lengths, B)
+    km = lsa.lsa_page_means(x["kv_off"], sb_off.to(DEV), x["k_idx"], B, x["max_len"])
+    return x, sb_off, km
+
+
+def test_layer_hi_full_recall_equals_flat_on_gpu():
+    # M * P >= L: every causal page is recalled, so HI picks exactly what the flat indexer picks
+    lengths = [6000, 3000, 1500]
+    x, sb_off, km = _hi_setup(lengths, M=64)
+    c = x["cfg"]
+    flat = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    hi = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"],
+                           sb_off=sb_off.to(DEV), k_mean=km)
+    assert torch.equal(flat[0], hi[0])
+    assert torch.equal(flat[1].view(torch.int16), hi[1].view(torch.int16))
+
+
+@pytest.mark.parametrize("B", [128, 16])
+def test_layer_hi_vs_oracle(B):
+    lengths = [40000, 25000, 9000]
+    x, sb_off, km = _hi_setup(lengths, M=24, B=B, hi_min_len=20000)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], B)
+    assert np.array_equal(host(km), km_o)
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"],
+                                      sb_off=sb_off.to(DEV), k_mean=km)
+    w_idx, w_out, w_lse = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"],
+                                        o["q"], o["kv"], sb_off=sb_off.numpy(), k_mean=km_o)
+    _compare_layer(x, host(idx), host(out), host(lse), w_idx, w_out, w_lse, 2e-2,
+                   OracleRanking(o, c, sb_off.numpy(), km_o))
+    # the needle pages are recalled and their needles picked
+    g_idx = host(idx)
+    for b, picks in enumerate(x["needles"]):
+        if x["lengths"][b] >= c["hi_min_len"]:
+            assert set(picks) <= set(g_idx[b].tolist())
+
+
+def test_cli_reuse_layer():
+    x = synth.decode_batch([7000, 3000], device=DEV, seed=9, needles=4)
+    c = x["cfg"]
+    o = oracle_inputs(x)
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    reuse = dict(c, is_owner=0)
+    # with the owner's own q / kv the reuse layer reproduces the owner's output bit for bit
+    _, out2, lse2 = lsa.lsa_layer_fwd(reuse, rows_of(x), x["q"], x["kv"], idx=idx.clone())
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
+    # with its own q / kv and the oracle's index set it matches the oracle's reuse layer
+    g = synth.generator(99, DEV)
+    q2 = synth.normal(tuple(x["q"].shape), 1.0, g, DEV, torch.bfloat16)
+    kv2 = synth.normal(tuple(x["kv"].shape), 1.0, g, DEV, torch.bfloat16)
+    w_idx, _, _ = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], o["q"],
+                                o["kv"])
+    _, out3, lse3 = lsa.lsa_layer_fwd(reuse, rows_of(x), q2, kv2, idx=torch.from_numpy(w_idx).to(DEV))
+    _, w_out3, w_lse3 = ref.layer_fwd(reuse, o["kv_off"], o["row_seq"], o["row_pos"], None, None, None, host(q2),
+                                      host(kv2), idx=w_idx)
+    assert_attn_close(host(out3), w_out3, host(lse3), w_lse3, 2e-2)
+
+
+def test_mtp_drafts_share_index_and_hi_gate():
+    lengths = [5000, 30000, 2000]
+    x, sb_off, km = _hi_setup(lengths, M=16, drafts=3, hi_min_len=20000)
+    c = x["cfg"]
+    o = oracle_inputs(x)
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], 128)
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"],
+                                      idx_row=x["idx_row"], sb_off=sb_off.to(DEV), k_mean=km)
+    g_idx = host(idx)
+    w_idx, w_out, w_lse = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"],
+                                        o["q"], o["kv"], idx_row=x["idx_row_host"].numpy(), sb_off=sb_off.numpy(),
+                                        k_mean=km_o)
+    assert np.all(g_idx[x["idx_row_host"].numpy() != np.arange(9)] == -1)   # drafts own no index row
+    ranking = OracleRanking(o, c, sb_off.numpy(), km_o)
+    assert_idx_sets_match(g_idx, w_idx, ranking.accept)
+    # every draft attends with its sequence's index set
+    same = np.array([np.array_equal(g_idx[x["idx_row_host"][r]], w_idx[x["idx_row_host"][r]]) for r in range(9)])
+    assert_attn_close(host(out)[same], w_out[same], host(lse)[same], w_lse[same], 2e-2)
+    for r in range(9):
+        if r % 3:
+            assert not torch.equal(out[r].view(torch.int16), out[r - r % 3].view(torch.int16))  # own q per draft

@@ -67,18 +67,28 @@ __device__ inline int compact_picks(const int32_t *pick_row, int k_sparse, const
         bool ok = s >= g.mid_lo && s < g.mid_hi && (i == 0 || pick_row[i - 1] != s);
         cnt += ok ? 1 : 0;
     }
-    scan_tmp[tid] = cnt;
+    // Exclusive scan of the per-thread counts: wave-level shuffles, then the wave totals.
+    const int lane = lane_id(), wave = tid >> 6, n_waves = nt >> 6;
+    int incl = cnt;
+    for (int o = 1; o < kWave; o <<= 1) {
+        int y = __shfl_up(incl, o, kWave);
+        if (lane >= o)
+            incl += y;
+    }
+    if (lane == kWave - 1)
+        scan_tmp[nt + 1 + wave] = incl;
     __syncthreads();
-    // exclusive scan (nt <= 512, serial over waves is fine: done once per block)
     if (tid == 0) {
         int acc = 0;
-        for (int i = 0; i < nt; ++i) {
-            int c = scan_tmp[i];
-            scan_tmp[i] = acc;
-            acc += c;
+        for (int i = 0; i < n_waves; ++i) {
+            int v = scan_tmp[nt + 1 + i];
+            scan_tmp[nt + 1 + i] = acc;
+            acc += v;
         }
         scan_tmp[nt] = acc;
     }
+    __syncthreads();
+    scan_tmp[tid] = scan_tmp[nt + 1 + wave] + incl - cnt;
     __syncthreads();
     int o = scan_tmp[tid];
     for (int i = i0; i < i0 + per && i < k_sparse; ++i) {
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(RowsDev rows, const floa
 {
     const int r = blockIdx.x, h = blockIdx.y;
     __shared__ int32_t sparse[kMaxSparse];
-    __shared__ int32_t scan_tmp[257];
+    __shared__ int32_t scan_tmp[256 + 1 + 4];
     __shared__ float z[kMaxSparse + 2048 + 64];
     __shared__ float qs[1024];
     __shared__ float red[8];
@@ -215,7 +225,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
     __shared__ __attribute__((aligned(16))) uint16_t kt[kRowsPerTile * kKStride];
     __shared__ __attribute__((aligned(16))) uint16_t vt[kDv * kVtStride];
     __shared__ int32_t sparse[kMaxSparse];
-    __shared__ int32_t scan_tmp[kAttnThreads + 1];
+    __shared__ int32_t scan_tmp[kAttnThreads + 1 + kAttnWaves];
     __shared__ int64_t tile_pos[kRowsPerTile];
 
     const RowInfo ri = row_info(rows, r);

@@ -7,10 +7,10 @@
 //
 // bf16 path (64 heads x 128 dims): one wave computes a [64 heads x 16 keys] tile with
 // v_mfma_f32_16x16x32_bf16 (4 head tiles x 4 depth steps).  The query's 64x128 block stays in
-// VGPRs for the whole wave; keys stream from HBM, 16 keys (4 KB) per tile, and the next tile is
-// loaded while the current one is multiplied.  The epilogue applies ReLU and the head weights in
+// VGPRs for the whole wave; keys stream from HBM, 16 keys (4 KB) per tile.  The epilogue applies ReLU and the head weights in
 // registers and reduces the 64 heads across the 4 lane groups with two xor shuffles; nothing but the
-// fp32 score (4 B per key) is written.  The depth order inside the MFMA is permuted so that each
+// fp32 score (4 B per key) is written.  Three tiles rotate through registers, so two 4 KB loads
+// per wave are in flight while the third tile is multiplied.  The depth order inside the MFMA is permuted so that each
 // lane reads one 64-byte contiguous run of a key row: lane group g owns depth [32g, 32g + 32) and
 // step ks feeds depth 32g + 8ks .. +8 (the same permutation is applied to q, so the dot product is
 // unchanged).
@@ -155,17 +155,9 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
         }
     };
 
-    u32x4 bcur[4], bnxt[4];
-    int64_t kcur = -1, knxt = -1;
-    if (first_tile < end_tile)
-        load_tile(first_tile, bcur, kcur);
-
-    for (int64_t tile = first_tile; tile < end_tile; tile += kWavesPerBlock) {
-        const int64_t next = tile + kWavesPerBlock;
-        if (next < end_tile)
-            load_tile(next, bnxt, knxt);
-
-        const bool any = __ballot(kcur >= 0) != 0;  // wave-uniform
+    // One tile: MFMAs, ReLU + head weights, reduction over the 4 lane groups, store.
+    auto compute = [&](int64_t tile, const u32x4 (&b)[4], int64_t key) {
+        const bool any = __ballot(key >= 0) != 0;  // wave-uniform
         float v = 0.0f;
         if (any) {
             f32x4 acc[4];
@@ -174,7 +166,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                 acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 bb = __builtin_bit_cast(bf16x8, bcur[ks]);
+                bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
                     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
@@ -200,12 +192,33 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                     out[p] = (p <= cm.last_page) ? v : -INFINITY;
             }
         } else if (g == 0 && c < c_end) {
-            out[c] = kcur >= 0 ? v : -INFINITY;
+            out[c] = key >= 0 ? v : -INFINITY;
         }
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            bcur[ks] = bnxt[ks];
-        kcur = knxt;
+    };
+
+    // Three register buffers: two tiles are in flight while the third is multiplied.
+    constexpr int64_t W = kWavesPerBlock;
+    u32x4 b0[4], b1[4], b2[4];
+    int64_t k0 = -1, k1 = -1, k2 = -1;
+    int64_t tile = first_tile;
+    if (tile < end_tile)
+        load_tile(tile, b0, k0);
+    if (tile + W < end_tile)
+        load_tile(tile + W, b1, k1);
+    for (; tile < end_tile; tile += 3 * W) {
+        if (tile + 2 * W < end_tile)
+            load_tile(tile + 2 * W, b2, k2);
+        compute(tile, b0, k0);
+        if (tile + W >= end_tile)
+            break;
+        if (tile + 3 * W < end_tile)
+            load_tile(tile + 3 * W, b0, k0);
+        compute(tile + W, b1, k1);
+        if (tile + 2 * W >= end_tile)
+            break;
+        if (tile + 4 * W < end_tile)
+            load_tile(tile + 4 * W, b1, k1);
+        compute(tile + 2 * W, b2, k2);
     }
 }
 

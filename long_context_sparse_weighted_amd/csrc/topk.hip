@@ -66,17 +66,6 @@ __device__ inline unsigned long long make_key(float s, int64_t c, int64_t n_cols
     return ((unsigned long long)float_order_key(s) << pos_bits) | (unsigned long long)(n_cols - 1 - c);
 }
 
-// Column c of row r is a candidate when its score is one and (page mode) its page slot is filled.
-__device__ inline bool col_candidate(const float *row, const int32_t *page_row, int P, int64_t c, float &s)
-{
-    s = row[c];
-    if (!is_candidate(s))
-        return false;
-    if (page_row && page_row[c / P] < 0)
-        return false;
-    return true;
-}
-
 __global__ void topk_init_kernel(TopkWs ws, int k, const uint8_t *row_mode, int want)
 {
     const int r = blockIdx.x;
@@ -120,15 +109,43 @@ __global__ __launch_bounds__(kPassThreads) void topk_pass_kernel(const float *__
     const int32_t *page_row = pages ? pages + (int64_t)r * M : nullptr;
     const int64_t c0 = (int64_t)blockIdx.x * kPassThreads * kPassElems;
     const unsigned long long dmask = (1ull << width) - 1;
-#pragma unroll 4
+    const int lane = lane_id();
+    // Load the whole batch first so the loads are all in flight together.
+    float sv[kPassElems];
+#pragma unroll
     for (int e = 0; e < kPassElems; ++e) {
         const int64_t c = c0 + (int64_t)e * kPassThreads + threadIdx.x;
-        float s;
-        if (c < n_cols && col_candidate(row, page_row, P, c, s)) {
-            unsigned long long key = make_key(s, c, n_cols, pos_bits);
-            if (consumed == 0 || (key >> (T - consumed)) == prefix)
-                atomicAdd(&lh[(key >> shift) & dmask], 1u);
+        sv[e] = c < n_cols ? row[c] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < kPassElems; ++e) {
+        const int64_t c = c0 + (int64_t)e * kPassThreads + threadIdx.x;
+        bool want = false;
+        uint32_t d = 0;
+        if (c < n_cols && is_candidate(sv[e]) && (!page_row || page_row[c / P] >= 0)) {
+            unsigned long long key = make_key(sv[e], c, n_cols, pos_bits);
+            if (consumed == 0 || (key >> (T - consumed)) == prefix) {
+                want = true;
+                d = (uint32_t)((key >> shift) & dmask);
+            }
         }
+        // Scores of one row crowd into a few bins: lanes that share a digit add it once
+        // (one LDS atomic per distinct digit, up to 8 of them); the rest add individually.
+        for (int it = 0; it < 8; ++it) {
+            unsigned long long act = __ballot(want);
+            if (act == 0)
+                break;
+            const int leader = __ffsll((long long)act) - 1;
+            const uint32_t dl = (uint32_t)__shfl((int)d, leader, kWave);
+            const bool same = want && d == dl;
+            const unsigned long long m = __ballot(same);
+            if (lane == leader)
+                atomicAdd(&lh[dl], (uint32_t)__popcll(m));
+            if (same)
+                want = false;
+        }
+        if (want)
+            atomicAdd(&lh[d], 1u);
     }
     __syncthreads();
     uint32_t *gh = ws.hist + (int64_t)r * kBins;
@@ -156,20 +173,41 @@ __global__ __launch_bounds__(kPassThreads) void topk_pass_kernel(const float *__
         mine += lh[kBins - 1 - (8 * t + i)];
     part[t] = mine;
     __syncthreads();
+    // Inclusive suffix sums of the per-thread parts (from the top digit down), in one wave.
+    __shared__ uint32_t above_part[kPassThreads];
+    if (t < kWave) {
+        uint32_t run = 0;
+        for (int base = 0; base < kPassThreads; base += kWave) {
+            uint32_t v = part[base + t];
+            uint32_t incl = v;
+            for (int o = 1; o < kWave; o <<= 1) {
+                uint32_t y = (uint32_t)__shfl_up((int)incl, o, kWave);
+                if (t >= o)
+                    incl += y;
+            }
+            above_part[base + t] = run + incl - v;  // exclusive: sum of parts before this one
+            run += (uint32_t)__shfl((int)incl, kWave - 1, kWave);
+        }
+    }
+    __syncthreads();
     if (t == 0) {
         uint32_t k_rem = st->k_rem;
-        uint32_t total = 0;
-        for (int i = 0; i < kPassThreads; ++i)
-            total += part[i];
+        const uint32_t total = above_part[kPassThreads - 1] + part[kPassThreads - 1];
         if (pass == 0 && total <= k_rem) {
             // At most K candidates: all of them are selected.
             st->done = 1;
         } else {
-            uint32_t above = 0;
-            int tt = 0;
-            while (above + part[tt] < k_rem)
-                above += part[tt++];
-            int d = kBins - 1 - 8 * tt;
+            // The part holding the K-th key: last part whose exclusive prefix is below k_rem.
+            int lo = 0, hi = kPassThreads - 1;
+            while (lo < hi) {
+                int mid = (lo + hi + 1) >> 1;
+                if (above_part[mid] < k_rem)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            uint32_t above = above_part[lo];
+            int d = kBins - 1 - 8 * lo;
             while (above + lh[d] < k_rem)
                 above += lh[d--];
             k_rem -= above;
@@ -181,6 +219,7 @@ __global__ __launch_bounds__(kPassThreads) void topk_pass_kernel(const float *__
         }
         st->ticket = 0;
     }
+    __syncthreads();
     // Clear the row histogram for the next pass.
     for (int i = threadIdx.x; i < kBins; i += blockDim.x)
         gh[i] = 0;
@@ -202,12 +241,18 @@ __global__ __launch_bounds__(kPassThreads) void topk_collect_kernel(const float 
     int32_t *list = ws.list + (int64_t)r * k;
     const int64_t c0 = (int64_t)blockIdx.x * kPassThreads * kPassElems;
     const int lane = lane_id();
+    float sv[kPassElems];
+#pragma unroll
     for (int e = 0; e < kPassElems; ++e) {
         const int64_t c = c0 + (int64_t)e * kPassThreads + threadIdx.x;
-        float s;
+        sv[e] = c < n_cols ? row[c] : -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < kPassElems; ++e) {
+        const int64_t c = c0 + (int64_t)e * kPassThreads + threadIdx.x;
         bool take = false;
-        if (c < n_cols && col_candidate(row, page_row, P, c, s)) {
-            unsigned long long key = make_key(s, c, n_cols, pos_bits);
+        if (c < n_cols && is_candidate(sv[e]) && (!page_row || page_row[c / P] >= 0)) {
+            unsigned long long key = make_key(sv[e], c, n_cols, pos_bits);
             take = consumed == 0 || (key >> (T - consumed)) >= prefix;
         }
         unsigned long long mask = __ballot(take);

@@ -17,16 +17,19 @@
 //   S^T[32 rows x 16 heads] = K_tile . Q^T       36 x v_mfma_f32_16x16x32_bf16 (Q^T lives in VGPRs)
 //   online softmax per head                      a lane owns one head; two xor shuffles
 //   O^T[512 x 16 heads] += V^T_tile . P^T        32 x v_mfma_f32_16x16x32_bf16 (128 accumulators)
-// P^T comes straight out of the S^T accumulator layout as the B operand.  Each tile is staged
-// with coalesced 16-byte loads into a row-major K tile in LDS; V^T is then built from it in LDS
-// (with the row permutation that matches the accumulator layout) using 16-byte stores that touch
-// all 32 banks, so every MFMA operand is one 16-byte LDS read.  The next tile's rows are loaded
-// into registers while the current one is multiplied.
+// P^T comes straight out of the S^T accumulator layout as the B operand.  Tiles are moved by the
+// gfx950 global-to-LDS DMA (global_load_lds_dwordx4) into one of two LDS buffers, so the next tile's
+// 1,152-byte rows stream in while the current tile is multiplied, without staging registers.  V^T
+// is then built from the K tile in LDS (with the row permutation that matches the accumulator
+// layout) using 16-byte stores that touch all 32 banks, so every MFMA operand is one 16-byte LDS
+// read.
 #include "lsa_kernels.hpp"
 
 namespace lsa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
@@ -37,6 +40,10 @@ constexpr int kAttnThreads = kAttnWaves * 64;
 constexpr int kHeadsPerBlock = kHeadsPerWave * kAttnWaves;
 constexpr int kMaxSparse = 4096;
 constexpr int kKStride = kDqk + 8;         // bf16 elements per LDS K row (1,168 B)
+constexpr int kChunksPerRow = kDqk / 8;    // 72 data chunks of 16 B per row
+constexpr int kSlotsPerRow = kKStride / 8; // 73 slots per LDS row (one of padding)
+constexpr int kDmaInstr = (32 * kSlotsPerRow + 63) / 64;  // 37 wave-wide 1 KB DMA writes per tile
+constexpr int kDmaSlots = kDmaInstr * 64;
 constexpr int kVtStride = kRowsPerTile + 8; // bf16 elements per LDS V^T row (80 B)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplitMerge = 64;
@@ -222,11 +229,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
 {
     const int split = blockIdx.x, r = blockIdx.y;
     const int h_block = blockIdx.z * kHeadsPerBlock;
-    __shared__ __attribute__((aligned(16))) uint16_t kt[kRowsPerTile * kKStride];
+    // Two K tiles (the next one arrives by DMA while the current one is used), the V^T tile, the
+    // compacted picks and the positions of the current tile's rows.
+    __shared__ __attribute__((aligned(16))) uint16_t kt[2][kDmaSlots * 8];
     __shared__ __attribute__((aligned(16))) uint16_t vt[kDv * kVtStride];
     __shared__ int32_t sparse[kMaxSparse];
     __shared__ int32_t scan_tmp[kAttnThreads + 1 + kAttnWaves];
-    __shared__ int64_t tile_pos[kRowsPerTile];
+    __shared__ int32_t tile_ok[2][kRowsPerTile];
 
     const RowInfo ri = row_info(rows, r);
     const SiRanges g = si_ranges(ri, k_sink, k_swa);
@@ -267,46 +276,38 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
     float l_run = 0.0f;       // this lane's rows only; the four lane groups are added at the end
     const float zs = scale * kLog2e;
 
-    // Staging: 32 rows x 72 chunks of 16 B = 2304 chunks over 512 threads.
-    constexpr int kChunksPerRow = kDqk / 8;
-    constexpr int kChunks = kRowsPerTile * kChunksPerRow;
-    constexpr int kPerThread = (kChunks + kAttnThreads - 1) / kAttnThreads;
-    u32x4 stage[kPerThread];
-
     auto tile_row_pos = [&](int tile, int row) -> int64_t {
         int j = tile * kRowsPerTile + row;
         return j < L.total ? sel_pos(L, sparse, j) : -1;
     };
-    auto load_stage = [&](int tile) {
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            int ch = tid + kAttnThreads * i;
-            int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
-            int64_t s = ch < kChunks ? tile_row_pos(tile, row) : -1;
-            stage[i] = s >= 0 ? *reinterpret_cast<const u32x4 *>(kv + (L.base + s) * kDqk + col * 8)
-                              : u32x4{0, 0, 0, 0};
+    // One tile = 32 rows x 73 16-byte slots (72 of data, one of padding against bank conflicts), moved
+    // by wave-wide 1 KB DMA writes: slot s of the tile receives chunk s % 73 of tile row s / 73.
+    // Padding slots and rows past the end of the list re-read an existing row of the sequence.
+    auto issue_tile = [&](int tile, uint16_t *buf) {
+        for (int jj = wave; jj < kDmaInstr; jj += kAttnWaves) {
+            const int slot = jj * kWave + lane;
+            const int row = slot / kSlotsPerRow, chunk = slot % kSlotsPerRow;
+            const int64_t pos = row < kRowsPerTile ? tile_row_pos(tile, row) : -1;
+            const int64_t grow = L.base + (pos >= 0 ? pos : 0);
+            const int cc = chunk < kChunksPerRow ? chunk : kChunksPerRow - 1;
+            const uint16_t *src = kv + grow * kDqk + cc * 8;
+            __builtin_amdgcn_global_load_lds((glb_void *)src, (lds_void *)(buf + jj * kWave * 8), 16, 0, 0);
         }
     };
 
     if (tile_lo < tile_hi)
-        load_stage(tile_lo);
+        issue_tile(tile_lo, kt[tile_lo & 1]);
 
     for (int tile = tile_lo; tile < tile_hi; ++tile) {
-        // Publish the staged tile (K rows as they are) ...
+        const uint16_t *ktc = kt[tile & 1];
+        int32_t *okc = tile_ok[tile & 1];
         if (tid < kRowsPerTile)
-            tile_pos[tid] = tile_row_pos(tile, tid);
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) {
-            int ch = tid + kAttnThreads * i;
-            if (ch < kChunks) {
-                int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
-                *reinterpret_cast<u32x4 *>(&kt[row * kKStride + col * 8]) = stage[i];
-            }
-        }
-        __syncthreads();
+            okc[tid] = tile_row_pos(tile, tid) >= 0 ? 1 : 0;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile has landed
+        __syncthreads();                                  // ... and every other wave's
         if (tile + 1 < tile_hi)
-            load_stage(tile + 1);
-        // ... and V^T from it: item (dv, block of 8 V^T columns) gathers 8 rows of one dv column
+            issue_tile(tile + 1, kt[(tile + 1) & 1]);
+        // V^T from the K tile: item (dv, block of 8 V^T columns) gathers 8 rows of one dv column
         // (consecutive lanes read consecutive dv of one row) and stores them as one 16-byte run.
 #pragma unroll
         for (int i = 0; i < (kDv * 4) / kAttnThreads; ++i) {
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
             uint32_t e[8];
 #pragma unroll
             for (int x = 0; x < 8; ++x)
-                e[x] = kt[vt_row(8 * blk + x) * kKStride + dv];
+                e[x] = ktc[vt_row(8 * blk + x) * kKStride + dv];
             u32x4 pk;
 #pragma unroll
             for (int x = 0; x < 4; ++x)
@@ -327,8 +328,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
         // S^T = K_tile . Q^T; lane (n, gq) ends with rows 4gq + i (sa) and 16 + 4gq + i (sb) of head n.
         f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
         {
-            const uint16_t *ra = &kt[n * kKStride + gq * 144];
-            const uint16_t *rb = &kt[(16 + n) * kKStride + gq * 144];
+            const uint16_t *ra = &ktc[n * kKStride + gq * 144];
+            const uint16_t *rb = &ktc[(16 + n) * kKStride + gq * 144];
 #pragma unroll
             for (int ks = 0; ks < 18; ++ks) {
                 u32x4 a0 = *reinterpret_cast<const u32x4 *>(ra + 8 * ks);
@@ -345,8 +346,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            z[i] = tile_pos[4 * gq + i] >= 0 ? sa[i] * zs : -INFINITY;
-            z[4 + i] = tile_pos[16 + 4 * gq + i] >= 0 ? sb[i] * zs : -INFINITY;
+            z[i] = okc[4 * gq + i] ? sa[i] * zs : -INFINITY;
+            z[4 + i] = okc[16 + 4 * gq + i] ? sb[i] * zs : -INFINITY;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -381,7 +382,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
                     __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __syncthreads();
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);

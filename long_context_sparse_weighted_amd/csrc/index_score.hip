@@ -10,10 +10,11 @@
 // VGPRs for the whole wave; keys stream from HBM, 16 keys (4 KB) per tile.  The epilogue applies ReLU and the head weights in
 // registers and reduces the 64 heads across the 4 lane groups with two xor shuffles; nothing but the
 // fp32 score (4 B per key) is written.  Three tiles rotate through registers, so two 4 KB loads
-// per wave are in flight while the third tile is multiplied.  The depth order inside the MFMA is permuted so that each
-// lane reads one 64-byte contiguous run of a key row: lane group g owns depth [32g, 32g + 32) and
-// step ks feeds depth 32g + 8ks .. +8 (the same permutation is applied to q, so the dot product is
-// unchanged).
+// per wave are in flight while the third tile is multiplied.  Step ks of the MFMA reads bytes
+// [64ks, 64ks + 64) of each of the 16 key rows (lane group g takes the 16 bytes at 64ks + 16g), so
+// each load instruction covers whole half-lines; two steps complete a 128-byte line while it is
+// still in L2.  Keys are read with ordinary (cached) loads: a streaming hint would drop the line
+// before its second half is read.
 //
 // fp32 path: one thread per key with the key row in VGPRs and q / w in LDS (small configs).
 #include "lsa_kernels.hpp"
@@ -98,18 +99,28 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                                                           const int64_t *sb_off, const int32_t *pages, int M, int P,
                                                           int B, float *__restrict__ scores, int64_t ld,
                                                           int64_t n_cols, int64_t cols_per_block,
-                                                          const uint8_t *row_mode, int want)
+                                                          const uint8_t *row_mode, int want, uint32_t *topk_hist)
 {
     const int r = blockIdx.y;
     if (row_mode && row_mode[r] != want)
         return;
+    // Optional fused first pass of the top-K that follows: a histogram of the top 11 bits of the
+    // order-preserving image of every score this block writes (one chunk = this block's columns).
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t part[256];
+    const bool fuse_hist = MODE != kModePageMean && topk_hist != nullptr;
+    if (fuse_hist) {
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+            lh[i] = 0;
+        __syncthreads();
+    }
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, sb_off, pages, r, M, P, B);
 
     const int lane = lane_id();
     const int n = lane & 15;  // key column within the tile / head row within an MFMA tile
-    const int g = lane >> 4;  // lane group: owns depth [32g, 32g+32) and heads 4g..4g+3 of each tile
+    const int g = lane >> 4;  // lane group: depth 32ks + 8g .. +8 of step ks; heads 4g..4g+3 of each tile
     const int wave = threadIdx.x >> 6;
 
     const int64_t c_begin = (int64_t)blockIdx.x * cols_per_block;
@@ -118,15 +129,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
         c_end = n_cols;
     float *out = scores + (int64_t)r * ld;
 
-    // A operands: q rows of this query, head mt*16 + n, depth 32g + 8ks .. +8.
+    // A operands: q rows of this query, head mt*16 + n, depth 32ks + 8g .. +8.
     u32x4 qa[4][4];
     const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 32);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            qa[mt][ks] = src[ks];
+            qa[mt][ks] = src[4 * ks];
     }
     // Head weights of the 16 heads whose dot products this lane ends up holding.
     float wv[4][4];
@@ -141,18 +152,30 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
     const int64_t first_tile = c_begin / kTile + wave;
     const int64_t end_tile = (c_end + kTile - 1) / kTile;
 
+    // A row with nothing to score writes -inf over its columns and issues no loads.
+    const bool row_has_keys = MODE == kModePageMean ? cm.nsb > 0 : cm.lo < cm.hi;
+    if (!row_has_keys) {
+        if (fuse_hist)
+            store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
+        if (MODE == kModePageMean) {
+            for (int64_t p = c_begin / cm.G + threadIdx.x; p < (c_end + cm.G - 1) / cm.G && p < ld; p += blockDim.x)
+                out[p] = -INFINITY;
+        } else {
+            for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
+                out[c] = -INFINITY;
+        }
+        return;
+    }
+    // Columns without a score still load a row of the sequence (its first scored key), so every
+    // load is unconditional and the loads of later tiles stay in flight across iterations.
+    const int64_t safe_key = MODE == kModePageMean ? cm.base : cm.base + cm.lo;
     auto load_tile = [&](int64_t tile, u32x4 (&b)[4], int64_t &key) {
         key = col_key<MODE>(cm, tile * kTile + n);
-        if (key >= 0) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(keys + key * kDim + g * 32);
+        const int64_t row_k = key >= 0 ? key : safe_key;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(keys + row_k * kDim + g * 8);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                b[ks] = __builtin_nontemporal_load(src + ks);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                b[ks] = u32x4{0, 0, 0, 0};
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            b[ks] = src[4 * ks];
     };
 
     // One tile: MFMAs, ReLU + head weights, reduction over the 4 lane groups, store.
@@ -183,16 +206,20 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
         }
         const int64_t c = tile * kTile + n;
         if (MODE == kModePageMean) {
-            // Sum the G sub-blocks of each page (they are G consecutive columns of this tile).
+            // Sum the G sub-blocks of each page (they are G consecutive columns of this tile); a
+            // sub-block that does not exist adds nothing.
+            if (key < 0)
+                v = 0.0f;
             for (int o = 1; o < cm.G; o <<= 1)
                 v += __shfl_xor(v, o, kWave);
-            if (g == 0 && (n % cm.G) == 0) {
-                int64_t p = c / cm.G;
-                if (p < ld)
-                    out[p] = (p <= cm.last_page) ? v : -INFINITY;
-            }
-        } else if (g == 0 && c < c_end) {
+            // (every lane group holds the same sums; all of them store, without branching)
+            const int64_t p = c / cm.G;
+            if ((n % cm.G) == 0 && p < ld)
+                out[p] = (p <= cm.last_page) ? v : -INFINITY;
+        } else if (c < c_end) {
             out[c] = key >= 0 ? v : -INFINITY;
+            if (fuse_hist && g == 0 && key >= 0)
+                atomicAdd(&lh[float_order_key(v) >> 21], 1u);
         }
     };
 
@@ -201,24 +228,21 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
     u32x4 b0[4], b1[4], b2[4];
     int64_t k0 = -1, k1 = -1, k2 = -1;
     int64_t tile = first_tile;
-    if (tile < end_tile)
-        load_tile(tile, b0, k0);
-    if (tile + W < end_tile)
-        load_tile(tile + W, b1, k1);
+    load_tile(tile, b0, k0);
+    load_tile(tile + W, b1, k1);
     for (; tile < end_tile; tile += 3 * W) {
-        if (tile + 2 * W < end_tile)
-            load_tile(tile + 2 * W, b2, k2);
+        load_tile(tile + 2 * W, b2, k2);
         compute(tile, b0, k0);
-        if (tile + W >= end_tile)
-            break;
-        if (tile + 3 * W < end_tile)
-            load_tile(tile + 3 * W, b0, k0);
-        compute(tile + W, b1, k1);
-        if (tile + 2 * W >= end_tile)
-            break;
-        if (tile + 4 * W < end_tile)
-            load_tile(tile + 4 * W, b1, k1);
-        compute(tile + 2 * W, b2, k2);
+        load_tile(tile + 3 * W, b0, k0);
+        if (tile + W < end_tile)
+            compute(tile + W, b1, k1);
+        load_tile(tile + 4 * W, b1, k1);
+        if (tile + 2 * W < end_tile)
+            compute(tile + 2 * W, b2, k2);
+    }
+    if (fuse_hist) {
+        __syncthreads();
+        store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
     }
 }
 
@@ -304,29 +328,39 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
 static int64_t pick_cols_per_block(int64_t n_rows, int64_t n_cols)
 {
     int64_t total = n_rows * n_cols;
-    int64_t cpb = total / 4096;
+    int64_t cpb = total / 2048;
     cpb = (cpb + 63) / 64 * 64;
     if (cpb < 256)
         cpb = 256;
-    if (cpb > 8192)
-        cpb = 8192;
+    if (cpb > 16384)
+        cpb = 16384;
     return cpb;
+}
+
+TopkGeom score_geometry(int dtype, int n_rows, int64_t n_cols)
+{
+    if (dtype != 1)
+        return topk_geometry(n_rows, n_cols);
+    TopkGeom g;
+    g.chunk_elems = pick_cols_per_block(n_rows, n_cols);
+    g.n_chunks = (int)((n_cols + g.chunk_elems - 1) / g.chunk_elems);
+    return g;
 }
 
 template <int MODE>
 static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx, const float *w, const void *keys,
                               int n_heads, int head_dim, int k_sink, int k_swa, const int64_t *sb_off,
                               const int32_t *pages, int M, int P, int B, float *scores, int64_t ld, int64_t n_cols,
-                              RowGate gate, hipStream_t stream)
+                              RowGate gate, hipStream_t stream, uint32_t *topk_hist = nullptr)
 {
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
     if (dtype == 1) {
-        int64_t cpb = pick_cols_per_block(rows.n_rows, n_cols);
-        dim3 grid((unsigned)((n_cols + cpb - 1) / cpb), (unsigned)rows.n_rows);
+        const TopkGeom geo = score_geometry(dtype, rows.n_rows, n_cols);
+        dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
         hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
-                           (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols, cpb,
-                           gate.row_mode, gate.want);
+                           (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
+                           geo.chunk_elems, gate.row_mode, gate.want, topk_hist);
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
         dim3 grid((unsigned)((threads_cols + 255) / 256), (unsigned)rows.n_rows);
@@ -345,14 +379,14 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
 hipError_t launch_index_score(int dtype, const RowsDev &rows, int64_t max_kv_len, const void *q_idx, const float *w,
                               const void *k_idx, int n_heads, int head_dim, int k_sink, int k_swa,
                               const int32_t *pages, int M, int P, float *scores, int64_t ld, RowGate gate,
-                              hipStream_t stream)
+                              hipStream_t stream, uint32_t *topk_hist)
 {
     (void)max_kv_len;
     if (pages)
         return launch_mode<kModePaged>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, pages,
-                                       M, P, 1, scores, ld, ld, gate, stream);
+                                       M, P, 1, scores, ld, ld, gate, stream, topk_hist);
     return launch_mode<kModeFlat>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, nullptr,
-                                  0, 1, 1, scores, ld, ld, gate, stream);
+                                  0, 1, 1, scores, ld, ld, gate, stream, topk_hist);
 }
 
 hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len, const int64_t *sb_off,

@@ -126,6 +126,135 @@ def cpu_baseline(L=131072, rows=4, batch=32, seed=0):
                        f"{dt:.2f} s wall, extrapolated x{batch // rows} to the whole {batch}-row batch at L={L}")
 
 
+def time_layer(x, cfg, steps, warmup, idx_row=None, sb_off=None, k_mean=None, q=None, kv=None, idx=None):
+    """Seconds per lsa_layer_fwd call (events on the stream the library launches on)."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"])
+    n = x["row_pos"].numel()
+    layer = lsa.Layer(cfg, rows, torch.bfloat16, "cuda", use_hi=k_mean is not None)
+    if idx is None:
+        idx = torch.full((n, cfg["k_sparse"]), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, cfg["H"], cfg["Dv"]), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((n, cfg["H"]), dtype=torch.float32, device="cuda")
+    qq, kk = (x["q"] if q is None else q), (x["kv"] if kv is None else kv)
+    t = time_on_stream(lambda: layer(qq, kk, idx, out, lse, q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"],
+                                     idx_row=idx_row, sb_off=sb_off, k_mean=k_mean), steps, warmup)
+    return t, idx
+
+
+def bench_hi(steps, warmup, lengths=(262144, 524288, 1048576), batch=8):
+    """1M-context decode with HI (batch 8, P = B = 128, M = 1024) against the flat indexer on the same inputs."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    res = {}
+    for L in lengths:
+        x = synth.hi_decode(device="cuda", L=L, batch=batch)
+        c = x["cfg"]
+        sb_off = lsa.sb_offsets(x["lengths"], 128).to("cuda")
+        t_means = time_on_stream(lambda: lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, L), 3, 1)
+        km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, L)
+        t_hi, idx_hi = time_layer(x, c, steps, warmup, sb_off=sb_off, k_mean=km)
+        t_flat, idx_flat = time_layer(x, dict(c, hi_min_len=1 << 62), steps, warmup)
+        hi_bytes = batch * (L // 128 * 256 + 1024 * 128 * 256 + 2064 * 1152)
+        res[str(L)] = dict(hi_us=t_hi * 1e6, flat_us=t_flat * 1e6, speedup=t_flat / t_hi,
+                           page_means_build_us=t_means * 1e6, hi_alg_bytes=hi_bytes,
+                           hi_hbm_frac=hi_bytes / t_hi / HBM_PEAK,
+                           same_sets_rows=int((idx_hi == idx_flat).all(1).sum().item()))
+        log(f"[bench] HI L={L}: HI {t_hi * 1e6:.1f} us, flat {t_flat * 1e6:.1f} us ({t_flat / t_hi:.2f}x), "
+            f"mean build {t_means * 1e6:.0f} us")
+        del x, km
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill(steps, warmup):
+    """Chunked prefill: 8192 causal rows over a 131072-token prefix; owner layer and CLI reuse layer."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    x = synth.chunked_prefill_cli(device="cuda")
+    c = x["cfg"]
+    (q1, kv1), (q2, kv2) = x["layers"]
+    t_own, idx = time_layer(x, c, steps, warmup, q=q1, kv=kv1)
+    t_reuse, _ = time_layer(x, dict(c, is_owner=0), steps, warmup, q=q2, kv=kv2, idx=idx)
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"])
+    scores = torch.empty((8192, x["max_len"]), dtype=torch.float32, device="cuda")
+    t_idx = time_on_stream(lambda: lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], (16, 1024, 1024),
+                                                       scores=scores), steps, warmup)
+    t_attn = time_on_stream(lambda: lsa.lsa_hybrid_attn(rows, q2, kv2, 512, c["scale"], (16, 1024, 1024), idx),
+                            steps, warmup)
+    n_keys = sum(int(t) - 1040 + 1 for t in x["row_pos_host"].tolist())
+    idx_flops = n_keys * 64 * 128 * 2
+    attn_flops = 8192 * 2064 * 128 * (576 + 512) * 2
+    res = dict(owner_us=t_own * 1e6, reuse_us=t_reuse * 1e6, index_score_us=t_idx * 1e6, attention_us=t_attn * 1e6,
+               index_flops=idx_flops, index_mfma_frac=idx_flops / t_idx / BF16_PEAK,
+               attention_mfma_frac=attn_flops / t_attn / BF16_PEAK)
+    log(f"[bench] prefill: owner {t_own * 1e3:.2f} ms, reuse {t_reuse * 1e3:.2f} ms, indexer scoring "
+        f"{t_idx * 1e3:.2f} ms ({res['index_mfma_frac'] * 100:.1f}% MFMA), attention {t_attn * 1e3:.2f} ms "
+        f"({res['attention_mfma_frac'] * 100:.1f}% MFMA)")
+    return res
+
+
+def bench_ragged(steps, warmup):
+    """64 ragged sequences (4K-512K), 3 MTP drafts each sharing the first draft's index; HI for L >= 256K."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    x = synth.ragged_mtp(device="cuda")
+    c = x["cfg"]
+    sb_off = lsa.sb_offsets(x["lengths"], 128).to("cuda")
+    km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, x["max_len"])
+    t, _ = time_layer(x, c, steps, warmup, idx_row=x["idx_row"], sb_off=sb_off, k_mean=km)
+    n_hi = sum(1 for L in x["lengths"] if L >= 262144)
+    log(f"[bench] ragged MTP: {t * 1e6:.1f} us for 64 sequences (sum L = {sum(x['lengths'])}, {n_hi} on HI)")
+    return dict(latency_us=t * 1e6, sum_len=sum(x["lengths"]), hi_sequences=n_hi, queries_per_s=192 / t)
+
+
+def bench_tiny(steps, warmup):
+    import torch
+
+    import synth
+    x = synth.tiny_prefill(device="cuda")
+    t, _ = time_layer_fp32(x, steps, warmup)
+    log(f"[bench] tiny fp32 prefill: {t * 1e6:.1f} us")
+    return dict(latency_us=t * 1e6)
+
+
+def time_layer_fp32(x, steps, warmup):
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    c = x["cfg"]
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"])
+    layer = lsa.Layer(c, rows, torch.float32, "cuda")
+    n = x["row_pos"].numel()
+    idx = torch.full((n, c["k_sparse"]), -1, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, c["H"], c["Dv"]), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n, c["H"]), dtype=torch.float32, device="cuda")
+    return time_on_stream(lambda: layer(x["q"], x["kv"], idx, out, lse, q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"]),
+                          steps, warmup), idx
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size (for scaling the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(7)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
+    del a, b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +263,9 @@ def main():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--lengths", default="131072,1048576")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="decode", choices=["decode", "hi", "prefill", "ragged", "tiny", "all"],
+                    help="decode prints the metric line; the others print their own figures as one JSON line")
+    ap.add_argument("--copy-calibration", action="store_true", help="run a 1 GiB device copy first (PMC scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -141,6 +273,23 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+    if args.workload != "decode":
+        extra = {}
+        if args.workload in ("hi", "all"):
+            extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup)
+        if args.workload in ("prefill", "all"):
+            extra["chunked_prefill_cli"] = bench_prefill(args.steps, args.warmup)
+        if args.workload in ("ragged", "all"):
+            extra["ragged_mtp"] = bench_ragged(args.steps, args.warmup)
+        if args.workload in ("tiny", "all"):
+            extra["tiny_fp32_prefill"] = bench_tiny(args.steps, args.warmup)
+        if args.workload == "all":
+            extra["decode_sweep"] = {str(L): run_length(L, args.batch, args.steps, args.warmup)
+                                     for L in (4096, 16384, 65536, 131072, 262144, 1048576)}
+        print(json.dumps(extra), flush=True)
+        return
     lengths = [int(v) for v in args.lengths.split(",")]
     legs = [run_length(L, args.batch, args.steps, args.warmup) for L in lengths]
     head = legs[-1]

@@ -254,6 +254,31 @@ def test_attention_bf16_many_rows_single_split():
     assert_attn_close(host(out)[sel], want_o, host(lse)[sel], want_l, 2e-2)
 
 
+@pytest.mark.parametrize("repeat", [1, 40])
+def test_attention_bf16_late_dominant_logit(repeat):
+    # Latent rows whose last 64 dims (outside the value part) align with head 0's query give that head a
+    # logit ~100 nats (over 140 in log2 units) above everything in the first tile of each split: the
+    # softmax must still be exact.
+    lengths = [3000, 6000]
+    rows = [(0, 2999), (1, 5999), (1, 4000), (0, 1500)] * repeat
+    x = custom_rows(lengths, rows, seed=8)
+    q0 = x["q"][:, 0].float()
+    for r, (b, t) in enumerate(rows[:4]):
+        base = int(x["kv_off_host"][b])
+        for d in (0, 33, 70, 500):
+            x["kv"][base + t - d, 512:] = (48.0 * torch.sign(q0[r, 512:])).to(x["kv"].dtype)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx = _oracle_idx_for(x, 1024, np.random.default_rng(4))
+    out, lse = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], budget_of(c),
+                                   torch.from_numpy(idx).to(DEV))
+    sel = np.arange(0, len(rows), 7) if repeat > 1 else np.arange(len(rows))
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], o["row_seq"][sel], o["row_pos"][sel], o["q"][sel], o["kv"], 512,
+                                     c["scale"], 16, 1024, idx[sel])
+    assert np.max(want_l[:, 0]) > 80.0
+    log("dominant-logit attn max err", assert_attn_close(host(out)[sel], want_o, host(lse)[sel], want_l, 2e-2))
+
+
 # --------------------------------------------------------------------------------------------- layer
 
 

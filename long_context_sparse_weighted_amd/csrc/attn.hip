@@ -28,8 +28,6 @@
 namespace lsa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kDqk = 576;
 constexpr int kDv = 512;

@@ -85,12 +85,38 @@ __device__ inline int64_t col_key(const ColMap &m, int64_t c)
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 matrix-core kernel: 64 indexer heads x 128 dims.
+// bf16 matrix-core kernels: 64 indexer heads x 128 dims.
 
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kTile = 16;          // keys per MFMA tile
 constexpr int kWavesPerBlock = 4;
+
+// Rows 16 G .. 16 G + 15 form group G.  A group is scored by the multi-row kernel when all of its
+// rows exist, lie inside one sequence and pass the row gate: the rows then read the same keys.
+constexpr int kGroupRows = 16;
+
+__device__ inline bool group_uniform(const RowsDev &rows, const uint8_t *row_mode, int want, int grp)
+{
+    const int r0 = grp * kGroupRows;
+    if (r0 + kGroupRows > rows.n_rows)
+        return false;
+    const int32_t b = rows.row_seq[r0];
+    if (b < 0 || b >= rows.n_seq)
+        return false;
+    const int64_t L = rows.kv_off[b + 1] - rows.kv_off[b];
+    for (int i = 0; i < kGroupRows; ++i) {
+        const int r = r0 + i;
+        if (rows.row_seq[r] != b)
+            return false;
+        const int32_t t = rows.row_pos[r];
+        if (t < 0 || t >= L)
+            return false;
+        if (row_mode && row_mode[r] != want)
+            return false;
+    }
+    return true;
+}
 
 template <int MODE>
 __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
@@ -99,11 +125,14 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                                                           const int64_t *sb_off, const int32_t *pages, int M, int P,
                                                           int B, float *__restrict__ scores, int64_t ld,
                                                           int64_t n_cols, int64_t cols_per_block,
-                                                          const uint8_t *row_mode, int want, uint32_t *topk_hist)
+                                                          const uint8_t *row_mode, int want, uint32_t *topk_hist,
+                                                          int grouped)
 {
     const int r = blockIdx.y;
     if (row_mode && row_mode[r] != want)
         return;
+    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
+        return;  // scored by the multi-row kernel
     // Optional fused first pass of the top-K that follows: a histogram of the top 11 bits of the
     // order-preserving image of every score this block writes (one chunk = this block's columns).
     __shared__ uint32_t lh[kTopkBins];
@@ -247,6 +276,252 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 }
 
 // ------------------------------------------------------------------------------------------
+// Multi-row bf16 kernel (prefill): the 16 rows of a group share every key tile, so the keys are read
+// from HBM once per group instead of once per row and the work becomes matrix-core bound.
+//
+// Block = 8 waves; wave w owns rows 16 G + 2w and 16 G + 2w + 1 (both 64x128 query blocks stay in
+// VGPRs).  Keys arrive in stages of 128 (32 KB) by LDS DMA, double-buffered, one barrier per
+// stage.  Inside a stage the 16-byte chunk c of key k is stored at slot 16 k + (c ^ (k % 16)), so
+// the 16 lanes that read one MFMA operand hit 16 different bank groups.  The epilogue reduces the
+// two rows over the 4 lane groups with two shuffles (each row keeps half of the groups after the
+// first), and the fused top-K pass-0 histogram of each row lives in LDS as packed 16-bit counters
+// (a chunk holds at most 16384 columns), private to the wave that owns the row.
+
+// LDS add without return, issued directly: the compiler treats an LDS atomic as possibly touching
+// the buffer an LDS DMA is filling and would wait for the DMA first.  LDS operations of a wave
+// complete in order, so this extra operation only makes the compiler's own LDS waits stricter.
+__device__ inline void lds_add_u32(uint32_t *p, uint32_t v)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
+    asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
+constexpr int kGroupWaves = 8;
+constexpr int kGroupThreads = kGroupWaves * kWave;
+constexpr int kStageKeys = 128;
+constexpr int kStageTiles = kStageKeys / kTile;              // 8
+constexpr int kStageElems = kStageKeys * kDim;               // bf16 elements per stage (32 KB)
+constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 32 wave-wide 1 KB DMA writes
+constexpr int kMaxGroupChunk = 65535;                        // 16-bit histogram counters
+constexpr int kMinGroupedRows = 64;                          // fewer rows: the per-row kernel only
+
+__global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
+    RowsDev rows, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ keys,
+    int k_sink, int k_swa, float *__restrict__ scores, int64_t ld, int64_t n_cols, int64_t cols_per_block,
+    const uint8_t *row_mode, int want, uint32_t *topk_hist)
+{
+    const int chunk = blockIdx.x, grp = blockIdx.y;
+    if (!group_uniform(rows, row_mode, want, grp))
+        return;  // the per-row kernel scores these rows
+    // Two stage buffers as distinct objects: the compiler then knows that a DMA into one does not
+    // write what is being read from the other, and does not wait for it before those reads.
+    __shared__ __attribute__((aligned(16))) uint16_t stage0[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageElems];
+    __shared__ uint32_t hist[kGroupRows][kTopkBins / 2];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const bool fuse = topk_hist != nullptr;
+    const int rl0 = 2 * wave;  // local row index of this wave's first row
+    const int r0 = grp * kGroupRows + rl0;
+
+    // Column ranges (columns are below 2^31): every valid row scores [k_sink, hi_r) with hi_r the
+    // end of its mid region cut at L; lanes 0..15 of every wave take one row each and reduce.
+    const RowInfo ri0 = row_info(rows, r0);
+    const int L = (int)ri0.L;
+    const int64_t base = ri0.base;
+    auto row_hi = [&](int r) {
+        const RowInfo ri = row_info(rows, r);
+        const SiRanges gi = si_ranges(ri, k_sink, k_swa);
+        return (int)(gi.mid_hi < ri.L ? gi.mid_hi : ri.L);
+    };
+    const int lo = k_sink;
+    const int hiA = row_hi(r0), hiB = row_hi(r0 + 1);
+    int u_hi = row_hi(grp * kGroupRows + n);
+    for (int o = 1; o < 16; o <<= 1)
+        u_hi = max(u_hi, __shfl_xor(u_hi, o, kWave));
+    const int c_begin = chunk * (int)cols_per_block;
+    const int c_end = (int)min((int64_t)c_begin + cols_per_block, n_cols);
+    int st_first = 0, st_end = 0;  // stages of kStageKeys columns from c_begin that hold scores
+    {
+        const int a = max(lo, c_begin), b = min(u_hi, c_end);
+        if (a < b) {
+            st_first = (a - c_begin) / kStageKeys;
+            st_end = (b - c_begin + kStageKeys - 1) / kStageKeys;
+        }
+    }
+    const int cmp_lo = c_begin + st_first * kStageKeys;
+    const int cmp_hi = min(c_begin + st_end * kStageKeys, c_end);
+
+    // Columns outside the computed stages hold no score for any row of the group.
+    for (int rl = 0; rl < kGroupRows; ++rl) {
+        float *o = scores + (int64_t)(grp * kGroupRows + rl) * ld;
+        for (int64_t c = c_begin + tid; c < cmp_lo; c += kGroupThreads)
+            o[c] = -INFINITY;
+        for (int64_t c = cmp_hi + tid; c < c_end; c += kGroupThreads)
+            o[c] = -INFINITY;
+    }
+    if (fuse)
+        for (int i = lane; i < kTopkBins; i += kWave)
+            hist[rl0 + (i >> 10)][i & 1023] = 0;
+
+    if (st_first < st_end) {
+        // A operands of both rows, and the head weights of the 16 heads each lane ends up holding.
+        u32x4 qa[2][4][4];
+        float wv[2][4][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint16_t *qrow = q_idx + (int64_t)(r0 + j) * kHeads * kDim;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    qa[j][mt][ks] = src[4 * ks];
+                f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)(r0 + j) * kHeads + mt * 16 + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    wv[j][mt][i] = v[i];
+            }
+        }
+        // DMA j = wave + 8 jj of a stage fills slots 64 j .. 64 j + 63, i.e. keys 4 j .. 4 j + 3: this
+        // lane moves chunk c16 of key 4 wave + 32 jj + g (the same chunk for every jj).
+        const int kk0 = 4 * wave + g;
+        const int c16 = n ^ (kk0 & 15);
+        const uint16_t *kseq = keys + base * kDim;
+        auto issue_stage = [&](int st, uint16_t *buf) __attribute__((always_inline)) {
+            const int col0 = c_begin + st * kStageKeys;
+            const uint16_t *ks0 = kseq + (int64_t)col0 * kDim;
+            const int lim = L - 1 - col0;  // keys past the sequence re-read its last key
+#pragma unroll
+            for (int jj = 0; jj < kStageDma / kGroupWaves; ++jj) {
+                const int kk = min(kk0 + 32 * jj, lim);
+                __builtin_amdgcn_global_load_lds((glb_void *)(ks0 + kk * kDim + c16 * 8),
+                                                 (lds_void *)(buf + (wave + kGroupWaves * jj) * kWave * 8), 16, 0, 0);
+            }
+        };
+        float *outA = scores + (int64_t)r0 * ld;
+        float *outB = outA + ld;
+        const int my_hi = g < 2 ? hiA : hiB;
+        uint32_t *my_hist = hist[rl0 + (g < 2 ? 0 : 1)];
+
+        // One stage: wait for its DMA, start the next stage's into the other buffer, score 8 tiles.
+        auto run_stage = [&](int st, const uint16_t *buf, uint16_t *next) __attribute__((always_inline)) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA writes have landed
+            __syncthreads();                                  // ... and every other wave's
+            if (st + 1 < st_end)
+                issue_stage(st + 1, next);
+            const int col0 = c_begin + st * kStageKeys;
+            float *sA = outA + col0;
+            float *sB = outB + col0;
+            const int rel_lo = lo - col0, rel_hi = min(my_hi, c_end) - col0, rel_end = c_end - col0;
+            for (int tt = 0; tt < kStageTiles; ++tt) {
+                u32x4 b[4];
+                const uint16_t *krow = buf + (tt * kTile + n) * kDim;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+                f32x4 acc[2][4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, qa[j][mt][ks]), bb, acc[j][mt], 0, 0, 0);
+                }
+                float vA = 0.0f, vB = 0.0f;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        vA += wv[0][mt][i] * fmaxf(acc[0][mt][i], 0.0f);
+                        vB += wv[1][mt][i] * fmaxf(acc[1][mt][i], 0.0f);
+                    }
+                // Groups 0, 1 keep row A and take the other half of its partials from groups 2, 3;
+                // groups 2, 3 do the same for row B; then the pairs (0,1) and (2,3) combine.
+                float keep = g < 2 ? vA : vB;
+                const float send = g < 2 ? vB : vA;
+                keep += __shfl_xor(send, 32, kWave);
+                keep += __shfl_xor(keep, 16, kWave);
+                const int rel = tt * kTile + n;
+                const bool valid = rel >= rel_lo && rel < rel_hi;
+                const float val = valid ? keep : -INFINITY;
+                if (rel < rel_end) {
+                    if (g == 0)
+                        sA[rel] = val;
+                    else if (g == 2)
+                        sB[rel] = val;
+                    if (fuse && valid && (g & 1) == 0) {
+                        const uint32_t bin = float_order_key(keep) >> 21;
+                        lds_add_u32(&my_hist[bin >> 1], 1u << (16 * (bin & 1)));
+                    }
+                }
+            }
+        };
+        if (st_first & 1)
+            issue_stage(st_first, stage1);
+        else
+            issue_stage(st_first, stage0);
+        int st = st_first;
+        if (st & 1) {
+            run_stage(st, stage1, stage0);
+            ++st;
+        }
+        for (; st < st_end; st += 2) {
+            run_stage(st, stage0, stage1);
+            if (st + 1 < st_end)
+                run_stage(st + 1, stage1, stage0);
+        }
+    }
+    if (fuse) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // Suffix histograms of this wave's two rows: lane j sums bins [32 j, 32 j + 32).
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t *h = hist[rl0 + j];
+            uint32_t cnt[32];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t word = h[16 * lane + i];
+                cnt[2 * i] = word & 0xffffu;
+                cnt[2 * i + 1] = word >> 16;
+                tot += cnt[2 * i] + cnt[2 * i + 1];
+            }
+            uint32_t incl = tot;  // inclusive suffix over lanes >= this one
+            for (int o = 1; o < kWave; o <<= 1) {
+                const uint32_t y = (uint32_t)__shfl_down((int)incl, o, kWave);
+                if (lane + o < kWave)
+                    incl += y;
+            }
+            uint32_t acc = incl - tot;
+            uint32_t *out = topk_hist + ((int64_t)(r0 + j) * gridDim.x + chunk) * kTopkBins + 32 * lane;
+            uint32_t sfx[32];
+#pragma unroll
+            for (int b = 31; b >= 0; --b) {
+                acc += cnt[b];
+                sfx[b] = acc;
+            }
+#pragma unroll
+            for (int b4 = 0; b4 < 8; ++b4)
+                *reinterpret_cast<u32x4 *>(out + 4 * b4) =
+                    u32x4{sfx[4 * b4], sfx[4 * b4 + 1], sfx[4 * b4 + 2], sfx[4 * b4 + 3]};
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // fp32 VALU kernel (any n_heads <= 64, head_dim in {64, 128}); one thread per column.
 
 template <int DI, int MODE>
@@ -357,10 +632,17 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
         return hipSuccess;
     if (dtype == 1) {
         const TopkGeom geo = score_geometry(dtype, rows.n_rows, n_cols);
+        const bool grouped = MODE == kModeFlat && rows.n_rows >= kMinGroupedRows && geo.chunk_elems <= kMaxGroupChunk;
+        if (grouped) {
+            dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
+            hipLaunchKernelGGL(score_rows_kernel, ggrid, dim3(kGroupThreads), 0, stream, rows, (const uint16_t *)q_idx,
+                               w, (const uint16_t *)keys, k_sink, k_swa, scores, ld, n_cols, geo.chunk_elems,
+                               gate.row_mode, gate.want, topk_hist);
+        }
         dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
         hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
                            (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
-                           geo.chunk_elems, gate.row_mode, gate.want, topk_hist);
+                           geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
         dim3 grid((unsigned)((threads_cols + 255) / 256), (unsigned)rows.n_rows);

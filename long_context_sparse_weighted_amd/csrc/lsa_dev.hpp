@@ -12,6 +12,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 
+// Address spaces of the LDS-DMA builtin's operands.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 // Rows of a batch as the kernels see them (device pointers).
 struct RowsDev {
     const int64_t *kv_off;

@@ -68,6 +68,43 @@ def test_index_score_bf16_ragged_and_edges():
     assert np.all(np.isneginf(host(g)[-1]))  # a row outside its sequence scores nothing
 
 
+# Rows that exercise the multi-row (prefill) scoring kernel: groups of 16 rows of one sequence are
+# scored together, other groups row by row.  Groups: 0 uniform; 1 uniform with empty and edge mid
+# regions; 2 alternating sequences; 3 uniform in the second sequence; 4 uniform in a sequence too
+# short for any mid region; 5 with one row outside its sequence; then a partial group of 5 rows.
+GROUPED_LENGTHS = [6000, 3000, 700]
+GROUPED_ROWS = ([(0, t) for t in range(5984, 6000)]
+                + [(0, t) for t in (0, 1, 15, 16, 1039, 1040, 1041, 1042, 2000, 2001, 3000, 4500, 5999, 5998, 100,
+                                    3333)]
+                + [((0, 5000 + i) if i % 2 == 0 else (1, 2900 - 7 * i)) for i in range(16)]
+                + [(1, t) for t in range(2984, 3000)]
+                + [(2, t) for t in range(684, 700)]
+                + [(0, t) for t in range(3000, 3015)] + [(0, 6000)]
+                + [(0, t) for t in range(4000, 4005)])
+
+
+def test_index_score_bf16_grouped_rows():
+    x = custom_rows(GROUPED_LENGTHS, GROUPED_ROWS, attn=False, seed=31)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    ld = x["max_len"] + 37
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), ld=ld)
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=ld)
+    log("grouped bf16 scores worst err/tol", assert_scores_close(host(g), want))
+    assert np.all(np.isneginf(host(g)[64:80]))   # L = 700: no mid region anywhere
+
+
+def test_layer_bf16_grouped_rows():
+    x = custom_rows(GROUPED_LENGTHS, GROUPED_ROWS, seed=32)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
+    w_idx, w_out, w_lse = ref.layer_fwd(c, o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"],
+                                        o["q"], o["kv"])
+    _compare_layer(x, host(idx), host(out), host(lse), w_idx, w_out, w_lse, 2e-2, OracleRanking(o, c))
+
+
 def test_index_score_bf16_page_mapped():
     L = 9000
     x = custom_rows([L, 4000], [(0, L - 1), (0, 5000), (1, 3999)], attn=False)

@@ -228,8 +228,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
     const int split = blockIdx.x, r = blockIdx.y;
     const int h_block = blockIdx.z * kHeadsPerBlock;
     // Two K tiles (the next one arrives by DMA while the current one is used), the V^T tile, the
-    // compacted picks and the positions of the current tile's rows.
-    __shared__ __attribute__((aligned(16))) uint16_t kt[2][kDmaSlots * 8];
+    // compacted picks and the positions of the current tile's rows.  The two K tiles are distinct
+    // objects, each named statically below: the compiler can then tell that the DMA into one does
+    // not write the other and does not wait for it before reading the current tile.
+    __shared__ __attribute__((aligned(16))) uint16_t kt0[kDmaSlots * 8];
+    __shared__ __attribute__((aligned(16))) uint16_t kt1[kDmaSlots * 8];
     __shared__ __attribute__((aligned(16))) uint16_t vt[kDv * kVtStride];
     __shared__ int32_t sparse[kMaxSparse];
     __shared__ int32_t scan_tmp[kAttnThreads + 1 + kAttnWaves];
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
         const uint16_t *qh = q + ((int64_t)r * n_heads + (head_ok ? head : 0)) * kDqk + gq * 144;
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks)
-            qb[ks] = head_ok ? *reinterpret_cast<const u32x4 *>(qh + 8 * ks) : u32x4{0, 0, 0, 0};
+            qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 8 * ks);  // a missing head reads head 0, never stored
     }
     f32x4 o[32];  // O^T[dv = 16 mt + 4 gq + i][head n]
 #pragma unroll
@@ -293,18 +296,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
         }
     };
 
-    if (tile_lo < tile_hi)
-        issue_tile(tile_lo, kt[tile_lo & 1]);
-
-    for (int tile = tile_lo; tile < tile_hi; ++tile) {
-        const uint16_t *ktc = kt[tile & 1];
-        int32_t *okc = tile_ok[tile & 1];
+    auto run_tile = [&](int tile, const uint16_t *ktc, uint16_t *ktn, int32_t *okc) __attribute__((always_inline)) {
         if (tid < kRowsPerTile)
             okc[tid] = tile_row_pos(tile, tid) >= 0 ? 1 : 0;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile has landed
         __syncthreads();                                  // ... and every other wave's
         if (tile + 1 < tile_hi)
-            issue_tile(tile + 1, kt[(tile + 1) & 1]);
+            issue_tile(tile + 1, ktn);
         // V^T from the K tile: item (dv, block of 8 V^T columns) gathers 8 rows of one dv column
         // (consecutive lanes read consecutive dv of one row) and stores them as one 16-byte run.
 #pragma unroll
@@ -321,7 +319,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
                 pk[x] = e[2 * x] | (e[2 * x + 1] << 16);
             *reinterpret_cast<u32x4 *>(&vt[dv * kVtStride + 8 * blk]) = pk;
         }
-        __syncthreads();
+        lds_barrier();  // V^T complete (the next tile's DMA keeps running)
 
         // S^T = K_tile . Q^T; lane (n, gq) ends with rows 4gq + i (sa) and 16 + 4gq + i (sb) of head n.
         f32x4 sa = f32x4{0.f, 0.f, 0.f, 0.f}, sb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -380,6 +378,25 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
                     __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+
+
+
+    if (tile_lo < tile_hi) {
+        if (tile_lo & 1)
+            issue_tile(tile_lo, kt1);
+        else
+            issue_tile(tile_lo, kt0);
+    }
+    int tile = tile_lo;
+    if (tile < tile_hi && (tile & 1)) {
+        run_tile(tile, kt1, kt0, tile_ok[1]);
+        ++tile;
+    }
+    for (; tile < tile_hi; tile += 2) {
+        run_tile(tile, kt0, kt1, tile_ok[0]);
+        if (tile + 1 < tile_hi)
+            run_tile(tile + 1, kt1, kt0, tile_ok[1]);
     }
 
     float l_tot = l_run + __shfl_xor(l_run, 16, kWave);

@@ -143,6 +143,11 @@ __device__ inline bool is_candidate(float f)
 
 // ------------------------------------------------------------------------------- wave helpers
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete, then all waves
+// meet.  Unlike __syncthreads() it does not wait for outstanding global loads (an LDS DMA in
+// flight keeps running); the memory clobber keeps the compiler from moving accesses across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline int lane_id() { return __lane_id(); }
 
 __device__ inline float wave_sum(float v)

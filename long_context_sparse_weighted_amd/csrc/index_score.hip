@@ -19,11 +19,25 @@
 // fp32 path: one thread per key with the key row in VGPRs and q / w in LDS (small configs).
 #include "lsa_kernels.hpp"
 
+#include <type_traits>
+#include <utility>
+
 namespace lsa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 enum { kModeFlat = 0, kModePaged = 1, kModePageMean = 2 };
+
+// ReLU as one IEEE maximum (v_maximum3_f32); fmaxf would first canonicalize its operand.
+__device__ inline float relu(float x) { return __builtin_elementwise_maximum(x, 0.0f); }
+
+// Pins values that were loaded from memory: the compiler waits for those loads here, before
+// anything it cannot see (the counted LDS DMA) is in flight.
+template <typename T>
+__device__ inline void loaded_here(const T &v)
+{
+    asm volatile("" ::"v"(v));
+}
 
 // Per-row view of which key a column stands for.
 struct ColMap {
@@ -229,7 +243,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    v += wv[mt][i] * fmaxf(acc[mt][i], 0.0f);
+                    v += wv[mt][i] * relu(acc[mt][i]);
             v += __shfl_xor(v, 16, kWave);
             v += __shfl_xor(v, 32, kWave);
         }
@@ -276,6 +290,228 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 }
 
 // ------------------------------------------------------------------------------------------
+// Streaming bf16 kernel (decode): the same per-row work as score_mfma_kernel, with the keys moved by
+// LDS DMA.  A DMA instruction reads 1 KB of whole 128-byte lines (4 key rows), where an MFMA operand
+// load reads 64 bytes of each of 16 rows.  Each wave streams its own tiles through a private ring
+// of S 4 KB buffers (S - 1 tiles in flight), so no barrier is needed.  Chunk c of key k of a tile
+// sits at slot 16 k + (c ^ k): the 16 lanes reading one operand hit 16 different bank groups.
+//
+// The DMA is issued outside the compiler's view (it would otherwise wait for every DMA in flight
+// before each LDS read); the waits are counted here instead.  Vector memory operations of a wave
+// complete in issue order, and every step issues exactly 4 DMA instructions and one store (steps
+// past the wave's last tile re-score that tile and store the same value again), so "at most
+// 5 (S - 1) operations outstanding" means the DMA of the current tile has landed; while the ring is
+// filling, fewer stores follow it and the stricter 4 (S - 1) is used.
+
+#ifndef LSA_SCORE_RING
+#define LSA_SCORE_RING 4
+#endif
+constexpr int kScoreRing = LSA_SCORE_RING;
+
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane (lds_base wave-uniform).
+// Cache policy of the key stream: each key is read once, as whole lines (sc0 nt: streaming).
+#ifndef LSA_DMA_CPOL
+#define LSA_DMA_CPOL "sc0 nt"
+#endif
+__device__ inline void dma_16(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " LSA_DMA_CPOL ::"v"(src),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int MODE, int S>
+__global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
+                                                            const float *__restrict__ w,
+                                                            const uint16_t *__restrict__ keys, int k_sink, int k_swa,
+                                                            const int32_t *__restrict__ pages, int M, int P,
+                                                            float *__restrict__ scores, int64_t ld, int64_t n_cols,
+                                                            int64_t cols_per_block, const uint8_t *row_mode, int want,
+                                                            uint32_t *topk_hist, int grouped)
+{
+    static_assert(S >= 2 && 5 * (S - 1) < 64, "ring depth");
+    const int r = blockIdx.y;
+    if (row_mode && row_mode[r] != want)
+        return;
+    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
+        return;  // scored by the multi-row kernel
+    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t part[256];
+    __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
+    const bool fuse_hist = topk_hist != nullptr;
+    if (fuse_hist) {
+        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+            lh[i] = 0;
+        __syncthreads();
+    }
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges si = si_ranges(ri, k_sink, k_swa);
+    const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
+
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
+    const int64_t c_begin = (int64_t)blockIdx.x * cols_per_block;
+    const int64_t c_end = c_begin + cols_per_block < n_cols ? c_begin + cols_per_block : n_cols;
+    float *out = scores + (int64_t)r * ld;
+
+    const bool row_has_keys = cm.lo < cm.hi;
+    if (!row_has_keys) {
+        if (fuse_hist)
+            store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
+        for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
+            out[c] = -INFINITY;
+        return;
+    }
+    u32x4 qa[4][4];
+    const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qa[mt][ks] = src[4 * ks];
+    }
+    float wv[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wv[mt][i] = v[i];
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            loaded_here(qa[mt][ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            loaded_here(wv[mt][i]);
+    }
+
+    // This wave's tiles: groups of 4 consecutive tiles (64 columns) go to the waves in turn, so the
+    // block reads one dense window; step k of this wave is tile k % 4 of its group k / 4.  Steps
+    // past the wave's K use its last step's tile again (a tile past the chunk, in the last group,
+    // re-reads the chunk's last tile).
+    constexpr int W = kWavesPerBlock;
+    const int64_t chunk_tile = c_begin / kTile;
+    const int64_t end_tile = (c_end + kTile - 1) / kTile;
+    const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
+    const int64_t K = wave < n_groups ? 4 * ((n_groups - wave + W - 1) / W) : 0;
+    auto tile_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
+        return chunk_tile + 4 * ((k >> 2) * W + wave) + (k & 3);
+    };
+    const int64_t safe_key = cm.base + cm.lo;
+    const uint32_t ring_base =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&ring[0][wave][0];
+    constexpr uint32_t kSlotBytes = kWavesPerBlock * kTile * kDim * 2;
+    // Token position of the first column of a tile (-1: the tile holds no token).  A tile lies in
+    // one page (P is a multiple of 16), so the page table is read once per tile, by a scalar load.
+    auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
+        const int64_t c0 = tile * kTile;
+        if constexpr (MODE == kModeFlat) {
+            return c0;
+        } else {
+            // (columns and slots fit in 32 bits; readfirstlane keeps the index in scalar registers)
+            const int slot = __builtin_amdgcn_readfirstlane((int)(c0 / cm.P));
+            if (slot >= cm.M)
+                return -1;
+            const int64_t pg = pages[(int64_t)r * M + slot];
+            return pg < 0 ? -1 : pg * cm.P + (c0 - (int64_t)slot * cm.P);
+        }
+    };
+    auto key_of = [&](int64_t tp, int i) __attribute__((always_inline)) -> int64_t {
+        const int64_t sp = tp + i;
+        return (tp >= 0 && sp >= cm.lo && sp < cm.hi) ? cm.base + sp : -1;
+    };
+    // DMA instruction j of a tile fills bytes 1024 j .. 1024 j + 1023 of its buffer: key 4 j + g,
+    // chunk n ^ (4 j + g).
+    auto issue = [&](int64_t k) __attribute__((always_inline)) {
+        const int64_t tile = min(tile_of(k < K ? k : K - 1), end_tile - 1);
+        const int64_t tp = tile_pos(tile);
+        const uint32_t buf = ring_base + (uint32_t)(k % S) * kSlotBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int kk = 4 * j + g;
+            const int64_t key = key_of(tp, kk);
+            const int64_t row_k = key >= 0 ? key : safe_key;
+            dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
+        }
+    };
+    // Score of tile k for key n (every lane group ends with the same 16 values).
+    auto score_tile = [&](int64_t k) __attribute__((always_inline)) -> float {
+        issue(k + S - 1);
+        wait_vmcnt<4 * (S - 1)>();
+        const int64_t tp = tile_pos(tile_of(k));
+        const bool any = __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
+        float v = 0.0f;
+        if (any) {
+            const uint16_t *krow = &ring[k % S][wave][n * kDim];
+            u32x4 b[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+            f32x4 acc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
+                                                                      acc[mt], 0, 0, 0);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v += wv[mt][i] * relu(acc[mt][i]);
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+        }
+        return v;
+    };
+    if (K > 0) {
+        for (int k = 0; k < S - 1; ++k)
+            issue(k);
+        // Groups of 4 tiles: lane group g stores tile g's 16 scores, so one store instruction writes
+        // 256 contiguous bytes (whole lines).  The DMA waits above count DMA instructions only: a
+        // store between the DMA of a tile and its wait only makes the wait stricter.
+        for (int64_t k0 = 0; k0 < K; k0 += 4) {
+            const float v0 = score_tile(k0), v1 = score_tile(k0 + 1);
+            const float v2 = score_tile(k0 + 2), v3 = score_tile(k0 + 3);
+            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+            const int64_t tile = tile_of(k0 + g);
+            const int64_t c = tile * kTile + n;
+            const int64_t key = key_of(tile_pos(tile), n);
+            if (c < c_end) {
+                out[c] = key >= 0 ? v : -INFINITY;
+                if (fuse_hist && key >= 0)
+                    lds_add_u32(&lh[float_order_key(v) >> 21], 1u);
+            }
+        }
+        wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
+    }
+    if (fuse_hist) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Multi-row bf16 kernel (prefill): the 16 rows of a group share every key tile, so the keys are read
 // from HBM once per group instead of once per row and the work becomes matrix-core bound.
 //
@@ -286,15 +522,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 // two rows over the 4 lane groups with two shuffles (each row keeps half of the groups after the
 // first), and the fused top-K pass-0 histogram of each row lives in LDS as packed 16-bit counters
 // (a chunk holds at most 16384 columns), private to the wave that owns the row.
-
-// LDS add without return, issued directly: the compiler treats an LDS atomic as possibly touching
-// the buffer an LDS DMA is filling and would wait for the DMA first.  LDS operations of a wave
-// complete in order, so this extra operation only makes the compiler's own LDS waits stricter.
-__device__ inline void lds_add_u32(uint32_t *p, uint32_t v)
-{
-    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
-    asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
-}
 
 constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * kWave;
@@ -445,8 +672,8 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        vA += wv[0][mt][i] * fmaxf(acc[0][mt][i], 0.0f);
-                        vB += wv[1][mt][i] * fmaxf(acc[1][mt][i], 0.0f);
+                        vA += wv[0][mt][i] * relu(acc[0][mt][i]);
+                        vB += wv[1][mt][i] * relu(acc[1][mt][i]);
                     }
                 // Groups 0, 1 keep row A and take the other half of its partials from groups 2, 3;
                 // groups 2, 3 do the same for row B; then the pairs (0,1) and (2,3) combine.
@@ -640,9 +867,14 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
                                gate.row_mode, gate.want, topk_hist);
         }
         dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
-        hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
-                           (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
-                           geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
+        if constexpr (MODE == kModePageMean)
+            hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
+                               (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
+                               geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
+        else
+            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing>), grid, dim3(256), 0, stream, rows,
+                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
+                               ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
         dim3 grid((unsigned)((threads_cols + 255) / 256), (unsigned)rows.n_rows);

@@ -244,8 +244,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     v += wv[mt][i] * relu(acc[mt][i]);
-            v += __shfl_xor(v, 16, kWave);
-            v += __shfl_xor(v, 32, kWave);
+            v = sum_xor32(sum_xor16(v));
         }
         const int64_t c = tile * kTile + n;
         if (MODE == kModePageMean) {
@@ -293,15 +292,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 // Streaming bf16 kernel (decode): the same per-row work as score_mfma_kernel, with the keys moved by
 // LDS DMA.  A DMA instruction reads 1 KB of whole 128-byte lines (4 key rows), where an MFMA operand
 // load reads 64 bytes of each of 16 rows.  Each wave streams its own tiles through a private ring
-// of S 4 KB buffers (S - 1 tiles in flight), so no barrier is needed.  Chunk c of key k of a tile
+// of S 4 KB buffers (up to S tiles in flight), so no barrier is needed.  Chunk c of key k of a tile
 // sits at slot 16 k + (c ^ k): the 16 lanes reading one operand hit 16 different bank groups.
 //
 // The DMA is issued outside the compiler's view (it would otherwise wait for every DMA in flight
 // before each LDS read); the waits are counted here instead.  Vector memory operations of a wave
-// complete in issue order, and every step issues exactly 4 DMA instructions and one store (steps
-// past the wave's last tile re-score that tile and store the same value again), so "at most
-// 5 (S - 1) operations outstanding" means the DMA of the current tile has landed; while the ring is
-// filling, fewer stores follow it and the stricter 4 (S - 1) is used.
+// complete in issue order and every step issues exactly 4 DMA instructions (steps past the wave's
+// last tile re-read that tile), so when tile k is due exactly the 4 (S - 1) DMA instructions of
+// tiles k + 1 .. k + S - 1 follow its own; score stores in between only make "at most 4 (S - 1)
+// outstanding" stricter.
 
 #ifndef LSA_SCORE_RING
 #define LSA_SCORE_RING 4
@@ -317,6 +316,15 @@ __device__ inline void dma_16(const void *src, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " LSA_DMA_CPOL ::"v"(src),
                  "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// The same from a wave-uniform base (SGPR pair) plus a per-lane 32-bit byte offset: no per-lane
+// 64-bit address arithmetic.  (The kernels using these do not otherwise use M0.)
+__device__ inline void dma_16s(const void *sbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 " LSA_DMA_CPOL ::"v"(voff),
+                 "s"(sbase), "s"(lds_base)
                  : "memory", "m0");
 }
 
@@ -342,12 +350,12 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         return;
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
         return;  // scored by the multi-row kernel
-    __shared__ uint32_t lh[kTopkBins];
+    __shared__ uint32_t lh[kTopkBins / 2];  // packed 16-bit counters: a chunk has at most 16384 columns
     __shared__ uint32_t part[256];
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
     const bool fuse_hist = topk_hist != nullptr;
     if (fuse_hist) {
-        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
+        for (int i = threadIdx.x; i < kTopkBins / 2; i += blockDim.x)
             lh[i] = 0;
         __syncthreads();
     }
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     const bool row_has_keys = cm.lo < cm.hi;
     if (!row_has_keys) {
         if (fuse_hist)
-            store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
+            store_suffix_hist<true>(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
         for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
             out[c] = -INFINITY;
         return;
@@ -434,33 +442,54 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         const int64_t sp = tp + i;
         return (tp >= 0 && sp >= cm.lo && sp < cm.hi) ? cm.base + sp : -1;
     };
+    // A tile is interior when all 16 of its columns hold keys (every tile but those at the ends of
+    // the scored range); the DMA, the scoring and the store then need no per-lane checks.
+    auto interior = [&](int64_t tp) __attribute__((always_inline)) {
+        return tp >= cm.lo && tp + kTile <= cm.hi;
+    };
     // DMA instruction j of a tile fills bytes 1024 j .. 1024 j + 1023 of its buffer: key 4 j + g,
-    // chunk n ^ (4 j + g).
+    // chunk n ^ (4 j + g); lane_off[j] is that key and chunk's byte offset from the tile's first key.
+    uint32_t lane_off[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        lane_off[j] = (uint32_t)((4 * j + g) * kDim * 2 + (n ^ (4 * j + g)) * 16);
     auto issue = [&](int64_t k) __attribute__((always_inline)) {
         const int64_t tile = min(tile_of(k < K ? k : K - 1), end_tile - 1);
         const int64_t tp = tile_pos(tile);
         const uint32_t buf = ring_base + (uint32_t)(k % S) * kSlotBytes;
+        if (interior(tp)) {
+            const uint16_t *kb = keys + (cm.base + tp) * kDim;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int kk = 4 * j + g;
-            const int64_t key = key_of(tp, kk);
-            const int64_t row_k = key >= 0 ? key : safe_key;
-            dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
+            for (int j = 0; j < 4; ++j)
+                dma_16s(kb, lane_off[j], buf + j * 1024);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kk = 4 * j + g;
+                const int64_t key = key_of(tp, kk);
+                const int64_t row_k = key >= 0 ? key : safe_key;
+                dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
+            }
         }
     };
-    // Score of tile k for key n (every lane group ends with the same 16 values).
-    auto score_tile = [&](int64_t k) __attribute__((always_inline)) -> float {
-        issue(k + S - 1);
-        wait_vmcnt<4 * (S - 1)>();
-        const int64_t tp = tile_pos(tile_of(k));
-        const bool any = __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
-        float v = 0.0f;
+    // Score of tile k (token position tp of its first column) for key n; every lane group ends with
+    // the same 16 values.
+    // The tile's operands move from its ring slot to registers first; once those LDS reads are done
+    // the slot takes the DMA of tile k + S, so all S slots are in flight during the arithmetic.
+    auto score_tile = [&](int64_t k, int64_t tp) __attribute__((always_inline)) -> float {
+        wait_vmcnt<4 * (S - 1)>();  // DMA(k) has landed: only DMA(k + 1 .. k + S - 1) may follow it
+        const bool any = interior(tp) || __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
+        u32x4 b[4];
         if (any) {
             const uint16_t *krow = &ring[k % S][wave][n * kDim];
-            u32x4 b[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
                 b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot k % S is free again
+        issue(k + S);
+        float v = 0.0f;
+        if (any) {
             f32x4 acc[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -478,28 +507,31 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     v += wv[mt][i] * relu(acc[mt][i]);
-            v += __shfl_xor(v, 16, kWave);
-            v += __shfl_xor(v, 32, kWave);
+            v = sum_xor32(sum_xor16(v));
         }
         return v;
     };
     if (K > 0) {
-        for (int k = 0; k < S - 1; ++k)
+        for (int k = 0; k < S; ++k)
             issue(k);
         // Groups of 4 tiles: lane group g stores tile g's 16 scores, so one store instruction writes
         // 256 contiguous bytes (whole lines).  The DMA waits above count DMA instructions only: a
         // store between the DMA of a tile and its wait only makes the wait stricter.
         for (int64_t k0 = 0; k0 < K; k0 += 4) {
-            const float v0 = score_tile(k0), v1 = score_tile(k0 + 1);
-            const float v2 = score_tile(k0 + 2), v3 = score_tile(k0 + 3);
+            const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
+            const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
+            const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
+            const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
             const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
-            const int64_t tile = tile_of(k0 + g);
-            const int64_t c = tile * kTile + n;
-            const int64_t key = key_of(tile_pos(tile), n);
+            const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
+            const int64_t c = tile_of(k0 + g) * kTile + n;
+            const bool valid = key_of(tp, n) >= 0;
             if (c < c_end) {
-                out[c] = key >= 0 ? v : -INFINITY;
-                if (fuse_hist && key >= 0)
-                    lds_add_u32(&lh[float_order_key(v) >> 21], 1u);
+                out[c] = valid ? v : -INFINITY;
+                if (fuse_hist && valid) {
+                    const uint32_t bin = float_order_key(v) >> 21;
+                    lds_add_u32(&lh[bin >> 1], 1u << (16 * (bin & 1)));
+                }
             }
         }
         wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
@@ -507,7 +539,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     if (fuse_hist) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
+        store_suffix_hist<true>(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
     }
 }
 
@@ -677,10 +709,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
                     }
                 // Groups 0, 1 keep row A and take the other half of its partials from groups 2, 3;
                 // groups 2, 3 do the same for row B; then the pairs (0,1) and (2,3) combine.
-                float keep = g < 2 ? vA : vB;
-                const float send = g < 2 ? vB : vA;
-                keep += __shfl_xor(send, 32, kWave);
-                keep += __shfl_xor(keep, 16, kWave);
+                const float keep = sum_xor16(sum_halves32(vA, vB));
                 const int rel = tt * kTile + n;
                 const bool valid = rel >= rel_lo && rel < rel_hi;
                 const float val = valid ? keep : -INFINITY;
@@ -827,6 +856,10 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
 }
 
 // Columns per block for the MFMA kernel: enough blocks to cover the chip a few times over.
+// (at most kMaxScoreChunk columns: the streaming kernel's LDS histogram counts in 16 bits)
+constexpr int64_t kMaxScoreChunk = 16384;
+static_assert(kMaxScoreChunk < 65536 && kMaxScoreChunk <= kMaxGroupChunk, "16-bit histogram counters");
+
 static int64_t pick_cols_per_block(int64_t n_rows, int64_t n_cols)
 {
     int64_t total = n_rows * n_cols;
@@ -834,8 +867,8 @@ static int64_t pick_cols_per_block(int64_t n_rows, int64_t n_cols)
     cpb = (cpb + 63) / 64 * 64;
     if (cpb < 256)
         cpb = 256;
-    if (cpb > 16384)
-        cpb = 16384;
+    if (cpb > kMaxScoreChunk)
+        cpb = kMaxScoreChunk;
     return cpb;
 }
 

@@ -159,6 +159,33 @@ __device__ inline void lds_add_u32(uint32_t *p, uint32_t v)
 
 __device__ inline int lane_id() { return __lane_id(); }
 
+// Cross-lane pair sums on the VALU with the CDNA4 lane swaps (no LDS round trip).
+// permlane32_swap(a, b) exchanges the upper 32 lanes of a with the lower 32 lanes of b, so the two
+// results add up to a[l] + a[l + 32] in lanes l < 32 and b[l - 32] + b[l] in lanes l >= 32.
+__device__ inline float sum_halves32(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Every lane: v[l] + v[l ^ 32].
+__device__ inline float sum_xor32(float v) { return sum_halves32(v, v); }
+// Every lane: v[l] + v[l ^ 16] (permlane16_swap exchanges odd 16-lane rows of a with even rows of b).
+__device__ inline float sum_xor16(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float max_xor32(float v)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float max_xor16(float v)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 __device__ inline float wave_sum(float v)
 {
     for (int o = 32; o > 0; o >>= 1)

@@ -42,7 +42,18 @@ constexpr int kTopkBins = 2048;
 
 // lh[] (kTopkBins LDS counters) -> out[b] = sum of lh[b'] for b' >= b (the keys in bin b or above).
 // Every thread of a block of `nthreads` (a multiple of 64 dividing kTopkBins) calls it; `part` is
-// LDS scratch of nthreads words.
+// LDS scratch of nthreads words.  PACKED: lh holds two 16-bit counters per word (bin b in half
+// b % 2 of word b / 2).
+template <bool PACKED = false>
+__device__ inline uint32_t hist_bin(const uint32_t *lh, int b)
+{
+    if constexpr (PACKED)
+        return (lh[b >> 1] >> (16 * (b & 1))) & 0xffffu;
+    else
+        return lh[b];
+}
+
+template <bool PACKED = false>
 __device__ inline void store_suffix_hist(const uint32_t *lh, uint32_t *part, uint32_t *__restrict__ out,
                                          int nthreads)
 {
@@ -50,7 +61,7 @@ __device__ inline void store_suffix_hist(const uint32_t *lh, uint32_t *part, uin
     const int per = kTopkBins / nthreads;
     uint32_t s = 0;
     for (int i = 0; i < per; ++i)
-        s += lh[t * per + i];
+        s += hist_bin<PACKED>(lh, t * per + i);
     part[t] = s;
     __syncthreads();
     if (t < kWave) {
@@ -73,7 +84,7 @@ __device__ inline void store_suffix_hist(const uint32_t *lh, uint32_t *part, uin
     __syncthreads();
     uint32_t acc = part[t];
     for (int i = per - 1; i >= 0; --i) {
-        acc += lh[t * per + i];
+        acc += hist_bin<PACKED>(lh, t * per + i);
         out[t * per + i] = acc;
     }
 }

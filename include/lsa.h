@@ -112,12 +112,14 @@ int lsa_page_recall_workspace_size(const lsa_rows_t *rows, int32_t P, int32_t M,
 
 /*
  * arg-topK ([paper] §2.2 Eq. 2; SI middle region [review] §2.1; HI stage 2 [paper] §3.3):
- * for each of n_rows rows of scores [n_rows, ld_scores], among the finite entries of columns
- * [0, n_cols) take the k best under (score desc, position asc) -- -0 equals +0, -inf is never
- * taken -- and write their positions ascending into idx [n_rows, k], padded with -1.
- * pages == NULL: the position of column c is c.  Otherwise pages [n_rows, M] (ascending page
- * lists, -1 = empty) maps column c to pages[r, c/P]*P + c%P, and columns of empty slots are not
- * candidates.  NaN scores are not candidates either.  Limits: 1 <= k <= 4096, n_cols < 2^31.
+ * for each of n_rows rows of scores [n_rows, ld_scores], among the entries of columns [0, n_cols)
+ * that are neither -inf nor NaN (+inf counts) take the k best under (score desc, position asc)
+ * -- -0 equals +0 -- and write their positions ascending into idx [n_rows, k], padded with -1
+ * when a row has fewer than k candidates.  pages == NULL: the position of column c is c.
+ * Otherwise pages [n_rows, M] (ascending page lists, -1 = empty) maps column c to
+ * pages[r, c/P]*P + c%P, and columns of empty slots are not candidates; P must be a multiple of
+ * 16.  Limits: 1 <= k <= 4096, n_cols < 2^31.  Workspace: lsa_topk_workspace_size() bytes,
+ * 256-byte aligned (may be NULL when that size is 0, i.e. n_cols <= 16384).
  */
 int lsa_topk(int32_t n_rows, const float *scores, int64_t ld_scores, int64_t n_cols, const int32_t *pages,
              int32_t M, int32_t P, int32_t k, int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);

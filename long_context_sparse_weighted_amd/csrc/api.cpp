@@ -132,18 +132,18 @@ LayerWs layer_ws_layout(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, bool
     if (cfg->is_owner) {
         w.row_mode = (uint8_t *)c.take((size_t)n);
         w.flat_scores = (float *)c.take(sizeof(float) * (size_t)n * (size_t)rows->max_kv_len);
-        // The flat and the HI token top-K share one workspace, chunked like their scoring grids.
-        int chunks = score_geometry(cfg->dtype, (int)n, rows->max_kv_len > 0 ? rows->max_kv_len : 1).n_chunks;
+        // The flat and the HI token top-K share one workspace.
+        size_t tk = topk_workspace_bytes((int)n, rows->max_kv_len > 0 ? rows->max_kv_len : 1, cfg->budget.k_sparse);
         if (use_hi) {
-            int hc = score_geometry(cfg->dtype, (int)n, (int64_t)cfg->M * cfg->P).n_chunks;
-            chunks = hc > chunks ? hc : chunks;
+            const size_t hk = topk_workspace_bytes((int)n, (int64_t)cfg->M * cfg->P, cfg->budget.k_sparse);
+            tk = hk > tk ? hk : tk;
         }
-        w.topk_ws = c.take(topk_workspace_bytes_geo((int)n, chunks));
+        w.topk_ws = c.take(tk);
         if (use_hi) {
             int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);
             w.page_scores = (float *)c.take(sizeof(float) * (size_t)n * (size_t)n_pages);
             w.pages = (int32_t *)c.take(sizeof(int32_t) * (size_t)n * (size_t)cfg->M);
-            w.page_topk_ws = c.take(topk_workspace_bytes((int)n, n_pages));
+            w.page_topk_ws = c.take(topk_workspace_bytes((int)n, n_pages, cfg->M));
             w.comp_scores = (float *)c.take(sizeof(float) * (size_t)n * (size_t)cfg->M * (size_t)cfg->P);
         }
     }
@@ -265,7 +265,7 @@ int lsa_page_recall_workspace_size(const lsa_rows_t *rows, int32_t P, int32_t M,
         return fail(LSA_ERR_INVALID, "P and M must be positive");
     Carver c(nullptr);
     c.take(sizeof(float) * (size_t)rows->n_rows * (size_t)ceil_div(rows->max_kv_len, P));
-    c.take(topk_workspace_bytes(rows->n_rows, ceil_div(rows->max_kv_len, P)));
+    c.take(topk_workspace_bytes(rows->n_rows, ceil_div(rows->max_kv_len, P), M));
     *bytes = c.used;
     return ok();
 }
@@ -297,7 +297,7 @@ int lsa_page_recall(int dtype, const lsa_rows_t *rows, const int64_t *sb_off, co
         return fail(LSA_ERR_INVALID, "workspace must be 256-byte aligned");
     Carver c(ws);
     float *ps_ws = (float *)c.take(sizeof(float) * (size_t)rows->n_rows * (size_t)n_pages);
-    void *tk = c.take(topk_workspace_bytes(rows->n_rows, n_pages));
+    void *tk = c.take(topk_workspace_bytes(rows->n_rows, n_pages, M));
     float *ps = page_scores ? page_scores : ps_ws;
     int64_t ld = page_scores ? ld_ps : n_pages;
     if (n_pages == 0 || rows->n_rows == 0) {
@@ -320,7 +320,7 @@ int lsa_topk_workspace_size(int32_t n_rows, int64_t n_cols, int32_t k, size_t *b
         return fail(LSA_ERR_INVALID, "bytes is NULL");
     if (n_rows < 0 || n_cols < 0 || k < 1)
         return fail(LSA_ERR_INVALID, "n_rows, n_cols >= 0 and k >= 1 required");
-    *bytes = topk_workspace_bytes(n_rows, n_cols);
+    *bytes = topk_workspace_bytes(n_rows, n_cols, k);
     return ok();
 }
 
@@ -340,13 +340,15 @@ int lsa_topk(int32_t n_rows, const float *scores, int64_t ld_scores, int64_t n_c
             return fail(LSA_ERR_INVALID, "page map needs M > 0 and P > 0");
         if ((int64_t)M * P < n_cols)
             return fail(LSA_ERR_INVALID, "page map covers %lld columns < n_cols", (long long)M * P);
+        if (P % 16 != 0)
+            return fail(LSA_ERR_UNSUPPORTED, "page size P must be a multiple of 16");
     }
     if (n_rows > 0 && (!idx || (n_cols > 0 && !scores)))
         return fail(LSA_ERR_INVALID, "scores and idx must be device pointers");
-    size_t need = topk_workspace_bytes(n_rows, n_cols);
-    if (ws_bytes < need || !ws)
+    size_t need = topk_workspace_bytes(n_rows, n_cols, k);
+    if (ws_bytes < need || (need && !ws))
         return fail(LSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
-    if (!aligned256(ws))
+    if (ws && !aligned256(ws))
         return fail(LSA_ERR_INVALID, "workspace must be 256-byte aligned");
     hipError_t e = launch_topk(n_rows, scores, ld_scores > 0 ? ld_scores : 1, n_cols, pages, M, P, k, idx, ws,
                                RowGate{nullptr, 0}, stream);
@@ -451,18 +453,14 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
     if (owner && rows->n_rows > 0) {
         e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
         const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
-        // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)); on the bf16 path the scoring epilogue
-        // also builds the first top-K histogram.
-        const bool fuse = cfg->dtype == LSA_BF16;
-        const TopkGeom fgeo = score_geometry(cfg->dtype, rows->n_rows, ld);
-        uint32_t *fhist = fuse ? topk_carve(lw.topk_ws, rows->n_rows, fgeo.n_chunks).hist : nullptr;
+        // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
         if (e == hipSuccess)
             e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                    cfg->head_dim_idx, bud.k_sink, bud.k_swa, nullptr, 0, 1, lw.flat_scores, ld,
-                                   RowGate{lw.row_mode, 1}, stream, fhist);
+                                   RowGate{lw.row_mode, 1}, stream);
         if (e == hipSuccess)
-            e = launch_topk_geo(rows->n_rows, lw.flat_scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, lw.topk_ws,
-                                fgeo, fuse, RowGate{lw.row_mode, 1}, stream);
+            e = launch_topk(rows->n_rows, lw.flat_scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, lw.topk_ws,
+                            RowGate{lw.row_mode, 1}, stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);
@@ -474,15 +472,13 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
             if (e == hipSuccess)
                 e = launch_topk(rows->n_rows, lw.page_scores, n_pages, n_pages, nullptr, 0, 1, cfg->M, lw.pages,
                                 lw.page_topk_ws, RowGate{lw.row_mode, 2}, stream);
-            const TopkGeom cgeo = score_geometry(cfg->dtype, rows->n_rows, n_comp);
-            uint32_t *chist = fuse ? topk_carve(lw.topk_ws, rows->n_rows, cgeo.n_chunks).hist : nullptr;
             if (e == hipSuccess)
                 e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                        cfg->head_dim_idx, bud.k_sink, bud.k_swa, lw.pages, cfg->M, cfg->P,
-                                       lw.comp_scores, n_comp, RowGate{lw.row_mode, 2}, stream, chist);
+                                       lw.comp_scores, n_comp, RowGate{lw.row_mode, 2}, stream);
             if (e == hipSuccess)
-                e = launch_topk_geo(rows->n_rows, lw.comp_scores, n_comp, n_comp, lw.pages, cfg->M, cfg->P,
-                                    bud.k_sparse, idx, lw.topk_ws, cgeo, fuse, RowGate{lw.row_mode, 2}, stream);
+                e = launch_topk(rows->n_rows, lw.comp_scores, n_comp, n_comp, lw.pages, cfg->M, cfg->P, bud.k_sparse,
+                                idx, lw.topk_ws, RowGate{lw.row_mode, 2}, stream);
         }
     }
     if (e == hipSuccess)

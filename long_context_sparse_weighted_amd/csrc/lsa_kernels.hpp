@@ -31,7 +31,10 @@ struct TopkWs {
 TopkGeom topk_geometry(int n_rows, int64_t n_cols);
 TopkWs topk_carve(void *ws, int n_rows, int n_chunks);
 size_t topk_workspace_bytes_geo(int n_rows, int n_chunks);
-size_t topk_workspace_bytes(int n_rows, int64_t n_cols);
+size_t topk_workspace_bytes(int n_rows, int64_t n_cols, int k);
+// k <= 4096: two-level selection (segments selected in registers, no per-chunk histograms; a
+// caller-chosen chunking and pre-computed pass-0 histograms are not used).
+bool topk_two_level(int k);
 hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages, int M,
                        int P, int k, int32_t *idx, void *ws, RowGate gate, hipStream_t stream);
 // Same, over a caller-chosen chunking; pass0_done: the pass-0 suffix histograms are already in ws.

@@ -84,8 +84,13 @@ size_t topk_workspace_bytes_geo(int n_rows, int n_chunks)
            2 * align_up(sizeof(uint32_t) * (size_t)n_chunks * n_rows);
 }
 
-size_t topk_workspace_bytes(int n_rows, int64_t n_cols)
+size_t topk2_workspace_bytes(int n_rows, int64_t n_cols, int k);
+bool topk_two_level(int k);
+
+size_t topk_workspace_bytes(int n_rows, int64_t n_cols, int k)
 {
+    if (topk_two_level(k))
+        return topk2_workspace_bytes(n_rows, n_cols > 0 ? n_cols : 1, k);
     return topk_workspace_bytes_geo(n_rows, topk_geometry(n_rows, n_cols).n_chunks);
 }
 
@@ -437,6 +442,364 @@ __global__ __launch_bounds__(kThreads) void topk_scatter_kernel(const float *__r
     }
 }
 
+// ----------------------------------------------------------------------------------- two-level
+//
+// For k <= kMaxLocalK the selection runs in two levels instead of the passes above.  A block holds a
+// segment of up to 64 * NT keys in registers (thread t holds positions 64 t .. 64 t + 63 of the
+// segment) and selects its best k under (key desc, position asc) by the same radix steps, on LDS
+// histograms.  Level 1 cuts each row into segments of kSeg scores and writes every segment's picks
+// (candidates: key and position, in position order, padded with key 0) -- the row's top k is among
+// them, since an element with fewer than k better elements in the row has fewer than k better
+// elements in its segment.  Further levels do the same on the candidate lists (whose order is
+// still position order) until one segment per row remains, whose picks are the result.  Scores
+// are read once.
+
+constexpr int kVpt = 64;                        // keys per thread
+constexpr int kSegThreads = 256;
+constexpr int kSeg = kVpt * kSegThreads;        // 16384
+constexpr int kMaxLocalK = 4096;
+
+// Exclusive prefix sums over threads (in thread order) of two counters, and their totals.
+// scratch: 2 * NT / 64 words of LDS.
+template <int NT>
+__device__ __attribute__((always_inline)) inline void block_scan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb, uint32_t &ta, uint32_t &tb,
+                                   uint32_t *scratch)
+{
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    uint32_t ia = a, ib = b;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t ya = (uint32_t)__shfl_up((int)ia, o, kWave), yb = (uint32_t)__shfl_up((int)ib, o, kWave);
+        if (lane >= o)
+            ia += ya, ib += yb;
+    }
+    if (lane == kWave - 1)
+        scratch[w] = ia, scratch[NW + w] = ib;
+    __syncthreads();
+    uint32_t pa = 0, pb = 0, sa = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint32_t xa = scratch[i], xb = scratch[NW + i];
+        if (i < w)
+            pa += xa, pb += xb;
+        sa += xa, sb += xb;
+    }
+    ea = pa + ia - a, eb = pb + ib - b, ta = sa, tb = sb;
+    __syncthreads();
+}
+
+struct Selection {
+    uint32_t prefix;    // fixed top `consumed` bits of the threshold
+    int consumed;
+    uint32_t k_rem;     // keys equal to the threshold that are picked (first in position order)
+    bool whole;         // keys whose top bits equal the prefix are all picked
+    bool all;           // every candidate is picked
+};
+
+// Radix select of the block's best k among the non-zero keys (0 = not a candidate).  The digit
+// histograms live in LDS as kCopies interleaved copies (bin b, copy c at hist[kCopies b + c]; lane l
+// adds to copy l % kCopies): keys of one row crowd into a few bins, and the copies spread the
+// atomics on such a bin over consecutive banks.  Keys that do not take part add to a per-lane
+// dummy word instead (no branch per key).
+constexpr int kCopies = 2;
+constexpr int kHistWords = kBins * kCopies + kWave;  // + one dummy word per lane
+constexpr int kStageWords = 2 * (kMaxLocalK + kWave);
+constexpr int kLdsWords = kHistWords > kStageWords ? kHistWords : kStageWords;
+
+template <int NT>
+__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[kVpt], uint32_t k,
+                                                                 uint32_t *hist, uint32_t *scratch, int *s_d,
+                                                                 uint32_t *s_above, uint32_t *s_bin)
+{
+    Selection sel{0u, 0, k, false, false};
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int m = 0; m < kVpt; ++m)
+        cnt += key[m] != 0 ? 1u : 0u;
+    uint32_t e0, e1, total, t1;
+    block_scan2<NT>(cnt, 0, e0, e1, total, t1, scratch);
+    if (total <= k) {
+        sel.all = true;
+        return sel;
+    }
+    const uint32_t lane = (uint32_t)lane_id();
+    const uint32_t copy = lane % kCopies, dummy = kBins * kCopies + lane;
+    constexpr int kPer = kBins / NT;  // bins owned by a thread in the suffix scan
+    // Cleared once here; afterwards every pass clears the words it has read.
+    for (int i = threadIdx.x; i < kBins * kCopies / 4; i += NT)
+        reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = digit_shift(pass);
+        const uint32_t dmask = (1u << digit_width(pass)) - 1;
+        // keys whose top `consumed` bits equal the prefix: (x & pmask) == pval (uniform scalars)
+        const uint32_t pmask = sel.consumed == 0 ? 0u : ~0u << (32 - sel.consumed);
+        const uint32_t pval = sel.consumed == 0 ? 0u : sel.prefix << (32 - sel.consumed);
+        // (Key 0, not a candidate, falls in pass-0 bin 0, below every candidate key: a digit
+        // below 3 is never selected while there are more than k candidates.)
+#pragma unroll
+        for (int m = 0; m < kVpt; ++m) {
+            const uint32_t x = key[m];
+            const bool take = (x & pmask) == pval;
+            atomicAdd(&hist[take ? kCopies * ((x >> shift) & dmask) + copy : dummy], 1u);
+        }
+        __syncthreads();
+        // Suffix sums (keys in bin b or above): thread t owns bins [kPer t, kPer t + kPer).
+        uint32_t hb[kPer];
+        uint32_t own = 0;
+        constexpr int kWords = kPer * kCopies;  // this thread's words, read (and cleared) 16 bytes at a time
+        static_assert(kWords % 4 == 0, "whole 16-byte words");
+        uint32_t wv[kWords];
+        uint4 *hw = reinterpret_cast<uint4 *>(hist + kWords * threadIdx.x);
+#pragma unroll
+        for (int q = 0; q < kWords / 4; ++q) {
+            const uint4 x = hw[q];
+            wv[4 * q] = x.x, wv[4 * q + 1] = x.y, wv[4 * q + 2] = x.z, wv[4 * q + 3] = x.w;
+            hw[q] = uint4{0u, 0u, 0u, 0u};  // ready for the next pass
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int c = 0; c < kCopies; ++c)
+                v += wv[kCopies * i + c];
+            hb[i] = v;
+            own += v;
+        }
+        uint32_t before, unused, sum_all, unused2;
+        block_scan2<NT>(own, 0, before, unused, sum_all, unused2, scratch);
+        uint32_t run = sum_all - before - own;  // keys in bins above this thread's
+#pragma unroll
+        for (int i = kPer - 1; i >= 0; --i) {
+            if (run < sel.k_rem && run + hb[i] >= sel.k_rem) {  // the bin holding the k_rem-th key
+                *s_d = kPer * threadIdx.x + i;
+                *s_above = run;
+                *s_bin = hb[i];
+            }
+            run += hb[i];
+        }
+        __syncthreads();
+        const int d = *s_d;
+        const uint32_t above = *s_above, bin = *s_bin;
+        __syncthreads();
+        sel.k_rem -= above;
+        sel.prefix = (sel.prefix << digit_width(pass)) | (uint32_t)d;
+        sel.consumed += digit_width(pass);
+        if (bin == sel.k_rem) {
+            sel.whole = true;
+            break;
+        }
+    }
+    return sel;
+}
+
+// Writes the picks of a selection, in position order, to stage_key / stage_li (key and index in
+// the segment) at slots 0 .. n - 1 and returns n; keys not picked go to per-lane dummy slots
+// stage[kMaxLocalK + lane].
+template <int NT>
+__device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&key)[kVpt], const Selection &sel,
+                                                              uint32_t *scratch, uint32_t *stage_key,
+                                                              uint32_t *stage_li, uint32_t first_li)
+{
+    // Thresholds on the whole key (uniform): picked for sure when x >= t_gt; a tie when x == t_eq.
+    //   all: every candidate;  whole: keys with top bits >= prefix;  otherwise T is exact
+    //   (32 bits fixed): x > T picked, x == T a tie.
+    //   (0xffffffff is a NaN pattern, mapped to key 0: no key equals it.)
+    uint32_t t_gt, t_eq = 0xffffffffu;
+    if (sel.all) {
+        t_gt = 1u;
+    } else if (sel.whole) {
+        t_gt = sel.prefix << (32 - sel.consumed);
+    } else {
+        t_gt = sel.prefix + 1u, t_eq = sel.prefix;  // consumed == 32: prefix is T
+    }
+    // Flags of this thread's keys as bit masks (bit m: key m).
+    uint64_t gbits = 0, ebits = 0;
+#pragma unroll
+    for (int m = 0; m < kVpt; ++m) {
+        gbits |= (uint64_t)(key[m] >= t_gt ? 1u : 0u) << m;
+        ebits |= (uint64_t)(key[m] == t_eq ? 1u : 0u) << m;
+    }
+    const uint32_t cg = (uint32_t)__popcll(gbits), ce = (uint32_t)__popcll(ebits);
+    uint32_t bg, be, tg, te;
+    block_scan2<NT>(cg, ce, bg, be, tg, te, scratch);
+    const uint32_t dummy = kMaxLocalK + (uint32_t)lane_id();
+#pragma unroll
+    for (int m = 0; m < kVpt; ++m) {
+        const bool g = (gbits >> m) & 1u, e = (ebits >> m) & 1u;
+        const bool pick = g || (e && be < sel.k_rem);
+        const uint32_t slot = pick ? bg + (be < sel.k_rem ? be : sel.k_rem) : dummy;
+        stage_key[slot] = key[m];
+        stage_li[slot] = first_li + m;
+        bg += g ? 1u : 0u;
+        be += e ? 1u : 0u;
+    }
+    return tg + (te < sel.k_rem ? te : sel.k_rem);
+}
+
+// One level.  SRC_SCORES: segment `seg` of row r is columns [seg * 64 NT, ...) of the scores (page
+// mapped when pages is given; P is a multiple of 16, so 16 aligned columns share a page);
+// otherwise candidates [seg * 64 NT, ...) of row r's list of n_in.  FINAL: the picks (positions)
+// go to idx[r][0 .. k), padded with -1; otherwise to the next list at [seg * k, seg * k + k),
+// padded with key 0.
+template <int NT, bool SRC_SCORES, bool FINAL>
+__global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict__ scores, int64_t ld, int64_t n_in,
+                                                         const int32_t *__restrict__ pages, int M, int P,
+                                                         const uint32_t *__restrict__ in_key,
+                                                         const int32_t *__restrict__ in_pos, int64_t in_ld, int k,
+                                                         uint32_t *__restrict__ out_key, int32_t *__restrict__ out_pos,
+                                                         int64_t out_ld, int32_t *__restrict__ idx,
+                                                         const uint8_t *row_mode, int want)
+{
+    const int seg = blockIdx.x, r = blockIdx.y;
+    if (row_mode && row_mode[r] != want)
+        return;
+    // LDS: the histograms, reused afterwards as the staging area of the picks.
+    __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
+    __shared__ uint32_t scratch[2 * NT / kWave];
+    __shared__ int s_d;
+    __shared__ uint32_t s_above, s_bin;
+    const int64_t seg_base = (int64_t)seg * (kVpt * NT);
+    const int64_t base = seg_base + (int64_t)kVpt * threadIdx.x;  // this thread's first element
+    const int32_t *page_row = pages ? pages + (int64_t)r * M : nullptr;
+    uint32_t key[kVpt];
+    if constexpr (SRC_SCORES) {
+        const float *row = scores + (int64_t)r * ld;
+        if (base + kVpt <= n_in && (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
+            const float4 *src = reinterpret_cast<const float4 *>(row + base);
+#pragma unroll
+            for (int q = 0; q < kVpt / 4; ++q) {
+                const float4 v = src[q];
+                key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
+                key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
+                key[4 * q + 2] = is_candidate(v.z) ? float_order_key(v.z) : 0u;
+                key[4 * q + 3] = is_candidate(v.w) ? float_order_key(v.w) : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kVpt; ++m) {
+                const int64_t c = base + m;
+                const float v = c < n_in ? row[c] : -INFINITY;
+                key[m] = is_candidate(v) ? float_order_key(v) : 0u;
+            }
+        }
+        if (page_row) {
+#pragma unroll
+            for (int q = 0; q < kVpt / 16; ++q) {
+                const int64_t c = base + 16 * q;
+                const bool ok = c < n_in && page_row[(uint32_t)c / (uint32_t)P] >= 0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    key[16 * q + i] = ok ? key[16 * q + i] : 0u;
+            }
+        }
+    } else {
+        const uint32_t *src = in_key + (int64_t)r * in_ld;
+        if (base + kVpt <= n_in) {
+            const uint4 *s4 = reinterpret_cast<const uint4 *>(src + base);
+#pragma unroll
+            for (int q = 0; q < kVpt / 4; ++q) {
+                const uint4 v = s4[q];
+                key[4 * q] = v.x, key[4 * q + 1] = v.y, key[4 * q + 2] = v.z, key[4 * q + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kVpt; ++m)
+                key[m] = base + m < n_in ? src[base + m] : 0u;
+        }
+    }
+    const Selection sel = block_select<NT>(key, (uint32_t)k, lds, scratch, &s_d, &s_above, &s_bin);
+    uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
+    __syncthreads();  // the histograms are no longer read
+    const uint32_t n_sel = block_emit<NT>(key, sel, scratch, stage_key, stage_li, (uint32_t)(kVpt * threadIdx.x));
+    __syncthreads();
+    // Copy-out in slot order (coalesced), with positions computed for the picks only.
+    for (int i = threadIdx.x; i < k; i += NT) {
+        int32_t pos = -1;
+        uint32_t kv = 0;
+        const int64_t c = seg_base + stage_li[i];
+        if ((uint32_t)i < n_sel && c < n_in) {  // (a pick is always below n_in: keys past it are 0)
+            kv = stage_key[i];
+            if constexpr (SRC_SCORES)
+                pos = page_row ? page_row[(uint32_t)c / (uint32_t)P] * P + (int32_t)((uint32_t)c % (uint32_t)P)
+                               : (int32_t)c;
+            else
+                pos = in_pos[(int64_t)r * in_ld + c];
+        }
+        if constexpr (FINAL) {
+            idx[(int64_t)r * k + i] = pos;
+        } else {
+            out_key[(int64_t)r * out_ld + (int64_t)seg * k + i] = kv;
+            out_pos[(int64_t)r * out_ld + (int64_t)seg * k + i] = pos;
+        }
+    }
+}
+
+// Candidates per row after level 1 and after one more level; row strides are rounded up to 4.
+static inline int64_t round4(int64_t x) { return (x + 3) & ~(int64_t)3; }
+static void topk2_sizes(int64_t n_cols, int k, int64_t &n_seg, int64_t &l0, int64_t &l1)
+{
+    n_seg = (n_cols + kSeg - 1) / kSeg;
+    l0 = n_seg * k;
+    l1 = ((l0 + kSeg - 1) / kSeg) * k;
+}
+
+size_t topk2_workspace_bytes(int n_rows, int64_t n_cols, int k)
+{
+    int64_t n_seg, l0, l1;
+    topk2_sizes(n_cols, k, n_seg, l0, l1);
+    if (n_seg <= 1)
+        return 0;
+    return 2 * align_up((size_t)n_rows * round4(l0) * 4) + 2 * align_up((size_t)n_rows * round4(l1) * 4);
+}
+
+bool topk_two_level(int k) { return k >= 1 && k <= kMaxLocalK; }
+
+static hipError_t launch_topk2(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages,
+                               int M, int P, int k, int32_t *idx, void *ws, RowGate gate, hipStream_t stream)
+{
+    int64_t n_seg, l0, l1;
+    topk2_sizes(n_cols, k, n_seg, l0, l1);
+    if (n_seg <= 1) {
+        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, true, true>), dim3(1, n_rows), dim3(kSegThreads), 0,
+                           stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, nullptr, nullptr, 0, idx,
+                           gate.row_mode, gate.want);
+        return hipGetLastError();
+    }
+    // Two candidate buffers (key, position) with row strides lda >= l0 and ldb >= l1, used in turn.
+    const int64_t lda = round4(l0), ldb = round4(l1);
+    char *p = (char *)ws;
+    uint32_t *key_a = (uint32_t *)p;
+    p += align_up((size_t)n_rows * lda * 4);
+    int32_t *pos_a = (int32_t *)p;
+    p += align_up((size_t)n_rows * lda * 4);
+    uint32_t *key_b = (uint32_t *)p;
+    p += align_up((size_t)n_rows * ldb * 4);
+    int32_t *pos_b = (int32_t *)p;
+    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, true, false>), dim3((unsigned)n_seg, n_rows),
+                       dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, key_a,
+                       pos_a, lda, nullptr, gate.row_mode, gate.want);
+    int64_t n_in = l0;
+    bool in_a = true;
+    while (n_in > kSeg) {  // reduce the candidate lists further
+        const int64_t segs = (n_in + kSeg - 1) / kSeg;
+        const int64_t n_out = segs * k;
+        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, false, false>), dim3((unsigned)segs, n_rows),
+                           dim3(kSegThreads), 0, stream, nullptr, 0, n_in, nullptr, 0, 1, in_a ? key_a : key_b,
+                           in_a ? pos_a : pos_b, in_a ? lda : ldb, k, in_a ? key_b : key_a, in_a ? pos_b : pos_a,
+                           in_a ? ldb : lda, nullptr, gate.row_mode, gate.want);
+        n_in = n_out;
+        in_a = !in_a;
+    }
+    const uint32_t *fk = in_a ? key_a : key_b;
+    const int32_t *fp = in_a ? pos_a : pos_b;
+    const int64_t fld = in_a ? lda : ldb;
+    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0, stream,
+                       nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx, gate.row_mode,
+                       gate.want);
+    return hipGetLastError();
+}
+
 // ----------------------------------------------------------------------------------- host
 
 hipError_t launch_topk_geo(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages, int M,
@@ -445,6 +808,8 @@ hipError_t launch_topk_geo(int n_rows, const float *scores, int64_t ld, int64_t 
 {
     if (n_rows == 0)
         return hipSuccess;
+    if (topk_two_level(k))
+        return launch_topk2(n_rows, scores, ld, n_cols > 0 ? n_cols : 0, pages, M, P, k, idx, ws_ptr, gate, stream);
     TopkWs ws = topk_carve(ws_ptr, n_rows, geo.n_chunks);
     const dim3 grid(geo.n_chunks, n_rows);
     const int64_t nc = n_cols > 0 ? n_cols : 0;

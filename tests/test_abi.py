@@ -70,16 +70,19 @@ def test_topk_validation(L):
     lib = L.lib()
     fake = ctypes.c_void_p(0x1000)
     sz = ctypes.c_size_t()
-    assert lib.lsa_topk_workspace_size(4, 100, 0, ctypes.byref(sz)) == L.LSA_ERR_INVALID
-    assert lib.lsa_topk_workspace_size(4, 100, 16, ctypes.byref(sz)) == L.LSA_OK and sz.value > 0
+    n = 100000  # several 16384-column segments: the selection needs candidate buffers
+    assert lib.lsa_topk_workspace_size(4, n, 0, ctypes.byref(sz)) == L.LSA_ERR_INVALID
+    assert lib.lsa_topk_workspace_size(4, 100, 16, ctypes.byref(sz)) == L.LSA_OK and sz.value == 0  # one segment
+    assert lib.lsa_topk_workspace_size(4, n, 16, ctypes.byref(sz)) == L.LSA_OK and sz.value > 0
     need = sz.value
-    assert lib.lsa_topk(4, fake, 100, 100, None, 0, 0, 0, fake, fake, need, None) == L.LSA_ERR_UNSUPPORTED
-    assert lib.lsa_topk(4, fake, 100, 100, None, 0, 0, 5000, fake, fake, need, None) == L.LSA_ERR_UNSUPPORTED
-    assert lib.lsa_topk(4, fake, 99, 100, None, 0, 0, 16, fake, fake, need, None) == L.LSA_ERR_INVALID
-    assert lib.lsa_topk(4, fake, 100, 100, None, 0, 0, 16, fake, fake, need - 1, None) == L.LSA_ERR_WORKSPACE
-    assert lib.lsa_topk(4, fake, 100, 100, None, 0, 0, 16, fake, ctypes.c_void_p(0x1010), need, None) == \
+    assert lib.lsa_topk(4, fake, n, n, None, 0, 0, 0, fake, fake, need, None) == L.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_topk(4, fake, n, n, None, 0, 0, 5000, fake, fake, need, None) == L.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_topk(4, fake, n - 1, n, None, 0, 0, 16, fake, fake, need, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_topk(4, fake, n, n, None, 0, 0, 16, fake, fake, need - 1, None) == L.LSA_ERR_WORKSPACE
+    assert lib.lsa_topk(4, fake, n, n, None, 0, 0, 16, fake, ctypes.c_void_p(0x1010), need, None) == \
         L.LSA_ERR_INVALID                                                                   # misaligned workspace
     assert lib.lsa_topk(4, fake, 100, 100, fake, 2, 16, 16, fake, fake, need, None) == L.LSA_ERR_INVALID  # M*P < n
+    assert lib.lsa_topk(4, fake, 100, 100, fake, 10, 24, 16, fake, fake, need, None) == L.LSA_ERR_UNSUPPORTED  # P%16
 
 
 def test_page_validation(L):

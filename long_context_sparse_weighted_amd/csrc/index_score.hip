@@ -139,24 +139,13 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                                                           const int64_t *sb_off, const int32_t *pages, int M, int P,
                                                           int B, float *__restrict__ scores, int64_t ld,
                                                           int64_t n_cols, int64_t cols_per_block,
-                                                          const uint8_t *row_mode, int want, uint32_t *topk_hist,
-                                                          int grouped)
+                                                          const uint8_t *row_mode, int want, int grouped)
 {
     const int r = blockIdx.y;
     if (row_mode && row_mode[r] != want)
         return;
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
         return;  // scored by the multi-row kernel
-    // Optional fused first pass of the top-K that follows: a histogram of the top 11 bits of the
-    // order-preserving image of every score this block writes (one chunk = this block's columns).
-    __shared__ uint32_t lh[kTopkBins];
-    __shared__ uint32_t part[256];
-    const bool fuse_hist = MODE != kModePageMean && topk_hist != nullptr;
-    if (fuse_hist) {
-        for (int i = threadIdx.x; i < kTopkBins; i += blockDim.x)
-            lh[i] = 0;
-        __syncthreads();
-    }
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, sb_off, pages, r, M, P, B);
@@ -198,8 +187,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
     // A row with nothing to score writes -inf over its columns and issues no loads.
     const bool row_has_keys = MODE == kModePageMean ? cm.nsb > 0 : cm.lo < cm.hi;
     if (!row_has_keys) {
-        if (fuse_hist)
-            store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
         if (MODE == kModePageMean) {
             for (int64_t p = c_begin / cm.G + threadIdx.x; p < (c_end + cm.G - 1) / cm.G && p < ld; p += blockDim.x)
                 out[p] = -INFINITY;
@@ -260,8 +247,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
                 out[p] = (p <= cm.last_page) ? v : -INFINITY;
         } else if (c < c_end) {
             out[c] = key >= 0 ? v : -INFINITY;
-            if (fuse_hist && g == 0 && key >= 0)
-                atomicAdd(&lh[float_order_key(v) >> 21], 1u);
         }
     };
 
@@ -281,10 +266,6 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
         load_tile(tile + 4 * W, b1, k1);
         if (tile + 2 * W < end_tile)
             compute(tile + 2 * W, b2, k2);
-    }
-    if (fuse_hist) {
-        __syncthreads();
-        store_suffix_hist(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
     }
 }
 
@@ -342,23 +323,15 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             const int32_t *__restrict__ pages, int M, int P,
                                                             float *__restrict__ scores, int64_t ld, int64_t n_cols,
                                                             int64_t cols_per_block, const uint8_t *row_mode, int want,
-                                                            uint32_t *topk_hist, int grouped)
+                                                            int grouped)
 {
-    static_assert(S >= 2 && 5 * (S - 1) < 64, "ring depth");
+    static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
     const int r = blockIdx.y;
     if (row_mode && row_mode[r] != want)
         return;
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
         return;  // scored by the multi-row kernel
-    __shared__ uint32_t lh[kTopkBins / 2];  // packed 16-bit counters: a chunk has at most 16384 columns
-    __shared__ uint32_t part[256];
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
-    const bool fuse_hist = topk_hist != nullptr;
-    if (fuse_hist) {
-        for (int i = threadIdx.x; i < kTopkBins / 2; i += blockDim.x)
-            lh[i] = 0;
-        __syncthreads();
-    }
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -373,8 +346,6 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 
     const bool row_has_keys = cm.lo < cm.hi;
     if (!row_has_keys) {
-        if (fuse_hist)
-            store_suffix_hist<true>(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
         for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
             out[c] = -INFINITY;
         return;
@@ -526,20 +497,10 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
             const int64_t c = tile_of(k0 + g) * kTile + n;
             const bool valid = key_of(tp, n) >= 0;
-            if (c < c_end) {
+            if (c < c_end)
                 out[c] = valid ? v : -INFINITY;
-                if (fuse_hist && valid) {
-                    const uint32_t bin = float_order_key(v) >> 21;
-                    lds_add_u32(&lh[bin >> 1], 1u << (16 * (bin & 1)));
-                }
-            }
         }
         wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
-    }
-    if (fuse_hist) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __syncthreads();
-        store_suffix_hist<true>(lh, part, topk_hist + ((int64_t)r * gridDim.x + blockIdx.x) * kTopkBins, 256);
     }
 }
 
@@ -551,9 +512,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 // VGPRs).  Keys arrive in stages of 128 (32 KB) by LDS DMA, double-buffered, one barrier per
 // stage.  Inside a stage the 16-byte chunk c of key k is stored at slot 16 k + (c ^ (k % 16)), so
 // the 16 lanes that read one MFMA operand hit 16 different bank groups.  The epilogue reduces the
-// two rows over the 4 lane groups with two shuffles (each row keeps half of the groups after the
-// first), and the fused top-K pass-0 histogram of each row lives in LDS as packed 16-bit counters
-// (a chunk holds at most 16384 columns), private to the wave that owns the row.
+// two rows over the 4 lane groups with two lane swaps (each row keeps half of the groups after the
+// first).
 
 constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * kWave;
@@ -561,13 +521,12 @@ constexpr int kStageKeys = 128;
 constexpr int kStageTiles = kStageKeys / kTile;              // 8
 constexpr int kStageElems = kStageKeys * kDim;               // bf16 elements per stage (32 KB)
 constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 32 wave-wide 1 KB DMA writes
-constexpr int kMaxGroupChunk = 65535;                        // 16-bit histogram counters
 constexpr int kMinGroupedRows = 64;                          // fewer rows: the per-row kernel only
 
 __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     RowsDev rows, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ keys,
     int k_sink, int k_swa, float *__restrict__ scores, int64_t ld, int64_t n_cols, int64_t cols_per_block,
-    const uint8_t *row_mode, int want, uint32_t *topk_hist)
+    const uint8_t *row_mode, int want)
 {
     const int chunk = blockIdx.x, grp = blockIdx.y;
     if (!group_uniform(rows, row_mode, want, grp))
@@ -576,14 +535,12 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     // write what is being read from the other, and does not wait for it before those reads.
     __shared__ __attribute__((aligned(16))) uint16_t stage0[kStageElems];
     __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageElems];
-    __shared__ uint32_t hist[kGroupRows][kTopkBins / 2];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = lane_id();
     const int n = lane & 15;
     const int g = lane >> 4;
-    const bool fuse = topk_hist != nullptr;
     const int rl0 = 2 * wave;  // local row index of this wave's first row
     const int r0 = grp * kGroupRows + rl0;
 
@@ -623,9 +580,6 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
         for (int64_t c = cmp_hi + tid; c < c_end; c += kGroupThreads)
             o[c] = -INFINITY;
     }
-    if (fuse)
-        for (int i = lane; i < kTopkBins; i += kWave)
-            hist[rl0 + (i >> 10)][i & 1023] = 0;
 
     if (st_first < st_end) {
         // A operands of both rows, and the head weights of the 16 heads each lane ends up holding.
@@ -665,7 +619,6 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
         float *outA = scores + (int64_t)r0 * ld;
         float *outB = outA + ld;
         const int my_hi = g < 2 ? hiA : hiB;
-        uint32_t *my_hist = hist[rl0 + (g < 2 ? 0 : 1)];
 
         // One stage: wait for its DMA, start the next stage's into the other buffer, score 8 tiles.
         auto run_stage = [&](int st, const uint16_t *buf, uint16_t *next) __attribute__((always_inline)) {
@@ -718,10 +671,6 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
                         sA[rel] = val;
                     else if (g == 2)
                         sB[rel] = val;
-                    if (fuse && valid && (g & 1) == 0) {
-                        const uint32_t bin = float_order_key(keep) >> 21;
-                        lds_add_u32(&my_hist[bin >> 1], 1u << (16 * (bin & 1)));
-                    }
                 }
             }
         };
@@ -738,41 +687,6 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
             run_stage(st, stage0, stage1);
             if (st + 1 < st_end)
                 run_stage(st + 1, stage1, stage0);
-        }
-    }
-    if (fuse) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // Suffix histograms of this wave's two rows: lane j sums bins [32 j, 32 j + 32).
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t *h = hist[rl0 + j];
-            uint32_t cnt[32];
-            uint32_t tot = 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t word = h[16 * lane + i];
-                cnt[2 * i] = word & 0xffffu;
-                cnt[2 * i + 1] = word >> 16;
-                tot += cnt[2 * i] + cnt[2 * i + 1];
-            }
-            uint32_t incl = tot;  // inclusive suffix over lanes >= this one
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t y = (uint32_t)__shfl_down((int)incl, o, kWave);
-                if (lane + o < kWave)
-                    incl += y;
-            }
-            uint32_t acc = incl - tot;
-            uint32_t *out = topk_hist + ((int64_t)(r0 + j) * gridDim.x + chunk) * kTopkBins + 32 * lane;
-            uint32_t sfx[32];
-#pragma unroll
-            for (int b = 31; b >= 0; --b) {
-                acc += cnt[b];
-                sfx[b] = acc;
-            }
-#pragma unroll
-            for (int b4 = 0; b4 < 8; ++b4)
-                *reinterpret_cast<u32x4 *>(out + 4 * b4) =
-                    u32x4{sfx[4 * b4], sfx[4 * b4 + 1], sfx[4 * b4 + 2], sfx[4 * b4 + 3]};
         }
     }
 }
@@ -855,59 +769,49 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
     return n_heads >= 1 && n_heads <= kHeads && (head_dim == 64 || head_dim == 128);
 }
 
-// Columns per block for the MFMA kernel: enough blocks to cover the chip a few times over.
-// (at most kMaxScoreChunk columns: the streaming kernel's LDS histogram counts in 16 bits)
-constexpr int64_t kMaxScoreChunk = 16384;
-static_assert(kMaxScoreChunk < 65536 && kMaxScoreChunk <= kMaxGroupChunk, "16-bit histogram counters");
+// Columns per block of the bf16 kernels: enough blocks to cover the chip a few times over.
+struct ScoreGeom {
+    int64_t chunk_elems;
+    int n_chunks;
+};
 
-static int64_t pick_cols_per_block(int64_t n_rows, int64_t n_cols)
+static ScoreGeom score_geometry(int64_t n_rows, int64_t n_cols)
 {
-    int64_t total = n_rows * n_cols;
-    int64_t cpb = total / 2048;
+    int64_t cpb = n_rows * n_cols / 2048;
     cpb = (cpb + 63) / 64 * 64;
     if (cpb < 256)
         cpb = 256;
-    if (cpb > kMaxScoreChunk)
-        cpb = kMaxScoreChunk;
-    return cpb;
-}
-
-TopkGeom score_geometry(int dtype, int n_rows, int64_t n_cols)
-{
-    if (dtype != 1)
-        return topk_geometry(n_rows, n_cols);
-    TopkGeom g;
-    g.chunk_elems = pick_cols_per_block(n_rows, n_cols);
-    g.n_chunks = (int)((n_cols + g.chunk_elems - 1) / g.chunk_elems);
-    return g;
+    if (cpb > 16384)
+        cpb = 16384;
+    return ScoreGeom{cpb, (int)((n_cols + cpb - 1) / cpb)};
 }
 
 template <int MODE>
 static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx, const float *w, const void *keys,
                               int n_heads, int head_dim, int k_sink, int k_swa, const int64_t *sb_off,
                               const int32_t *pages, int M, int P, int B, float *scores, int64_t ld, int64_t n_cols,
-                              RowGate gate, hipStream_t stream, uint32_t *topk_hist = nullptr)
+                              RowGate gate, hipStream_t stream)
 {
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
     if (dtype == 1) {
-        const TopkGeom geo = score_geometry(dtype, rows.n_rows, n_cols);
-        const bool grouped = MODE == kModeFlat && rows.n_rows >= kMinGroupedRows && geo.chunk_elems <= kMaxGroupChunk;
+        const ScoreGeom geo = score_geometry(rows.n_rows, n_cols);
+        const bool grouped = MODE == kModeFlat && rows.n_rows >= kMinGroupedRows;
         if (grouped) {
             dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
             hipLaunchKernelGGL(score_rows_kernel, ggrid, dim3(kGroupThreads), 0, stream, rows, (const uint16_t *)q_idx,
                                w, (const uint16_t *)keys, k_sink, k_swa, scores, ld, n_cols, geo.chunk_elems,
-                               gate.row_mode, gate.want, topk_hist);
+                               gate.row_mode, gate.want);
         }
         dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
         if constexpr (MODE == kModePageMean)
             hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
                                (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
-                               geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
+                               geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
         else
             hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
-                               ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want, topk_hist, grouped ? 1 : 0);
+                               ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
         dim3 grid((unsigned)((threads_cols + 255) / 256), (unsigned)rows.n_rows);
@@ -926,14 +830,14 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
 hipError_t launch_index_score(int dtype, const RowsDev &rows, int64_t max_kv_len, const void *q_idx, const float *w,
                               const void *k_idx, int n_heads, int head_dim, int k_sink, int k_swa,
                               const int32_t *pages, int M, int P, float *scores, int64_t ld, RowGate gate,
-                              hipStream_t stream, uint32_t *topk_hist)
+                              hipStream_t stream)
 {
     (void)max_kv_len;
     if (pages)
         return launch_mode<kModePaged>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, pages,
-                                       M, P, 1, scores, ld, ld, gate, stream, topk_hist);
+                                       M, P, 1, scores, ld, ld, gate, stream);
     return launch_mode<kModeFlat>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, nullptr,
-                                  0, 1, 1, scores, ld, ld, gate, stream, topk_hist);
+                                  0, 1, 1, scores, ld, ld, gate, stream);
 }
 
 hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len, const int64_t *sb_off,

@@ -148,15 +148,6 @@ __device__ inline bool is_candidate(float f)
 // flight keeps running); the memory clobber keeps the compiler from moving accesses across it.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// LDS add without return, issued directly: the compiler treats an LDS atomic as possibly touching
-// a buffer that an LDS DMA is filling and would wait for every DMA first.  LDS operations of a wave
-// complete in order, so this extra operation only makes the compiler's own LDS waits stricter.
-__device__ inline void lds_add_u32(uint32_t *p, uint32_t v)
-{
-    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)p;
-    asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
-}
-
 __device__ inline int lane_id() { return __lane_id(); }
 
 // Cross-lane pair sums on the VALU with the CDNA4 lane swaps (no LDS round trip).

@@ -630,6 +630,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
             float *sA = outA + col0;
             float *sB = outB + col0;
             const int rel_lo = lo - col0, rel_hi = min(my_hi, c_end) - col0, rel_end = c_end - col0;
+#pragma unroll 2  // (a full unroll spills)
             for (int tt = 0; tt < kStageTiles; ++tt) {
                 u32x4 b[4];
                 const uint16_t *krow = buf + (tt * kTile + n) * kDim;

@@ -42,6 +42,32 @@ def time_on_stream(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps * 1e-3  # seconds per call
 
 
+TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "score_stream_kernel_decode_b32_1m_traffic.md")
+TRAFFIC_L = 1048576
+TRAFFIC_SOURCES = ("index_score.hip", "lsa_dev.hpp", "lsa_kernels.hpp")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the scoring kernel from the committed rocprofv3 counter summary, or None
+    when the kernel's sources changed since the counters were taken (their hash differs)."""
+    import hashlib
+    try:
+        line = [v for v in open(TRAFFIC_PROFILE).read().splitlines() if v.startswith("traffic:")][0]
+    except (OSError, IndexError):
+        return None
+    f = dict(kv.split("=", 1) for kv in line.split()[1:])
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "long_context_sparse_weighted_amd", "csrc")
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != f["source_sha256"]:
+        return None
+    return round(float(f["fetch_kib"]) * float(f["fetch_scale"]) * 1024 +
+                 float(f["write_kib"]) * float(f["write_scale"]) * 1024)
+
+
 def run_length(L, batch, steps, warmup, seed=0):
     import torch
 
@@ -314,9 +340,11 @@ def main():
         "queries_per_s": round(args.batch / (head["latency_us"] * 1e-6), 1),
         "hbm_frac_layer": round(head["hbm_frac_layer"], 4),
         "mfma_frac_layer": round(head["flops"] / (head["latency_us"] * 1e-6) / BF16_PEAK, 4),
-        "roofline": {"kernel": "score_mfma_kernel (flat indexer scoring)", "bound": "hbm",
+        "roofline": {"kernel": "score_stream_kernel (flat indexer scoring)", "bound": "hbm",
                      "achieved": round(head["score_kernel_gbs"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(head["score_kernel_gbs"] * 1e9 / HBM_PEAK, 4), "traffic": None},
+                     "frac": round(head["score_kernel_gbs"] * 1e9 / HBM_PEAK, 4),
+                     "traffic": measured_traffic() if head["L"] == TRAFFIC_L else None,
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -426,6 +426,298 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
     }
 }
 
+// ------------------------------------------------------------------ bf16 kernel, 128 heads per block
+//
+// 4 waves (one per SIMD), 128 heads per block.  Per 32-row tile:
+//   QK: wave w computes S^T[32 rows x heads 32w .. 32w + 31] = K_tile . Q^T with 36 x
+//       v_mfma_f32_32x32x16_bf16 (its Q^T in VGPRs, K from the tile in LDS), applies the softmax
+//       weights and writes P (bf16) to LDS as P[head][row];
+//   PV: wave w computes O^T[dv 128w .. 128w + 127 x all 128 heads] += V^T . P^T with 32 x
+//       v_mfma_f32_32x32x16_bf16 (256 accumulators, in AGPRs); the V^T operands are read straight
+//       from the row-major K tile with the CDNA4 LDS transpose load (ds_read_b64_tr_b16) and the
+//       P^T operands from LDS.
+// Every wave reads the K tile once, the V^T of its 128 value columns and P once: about a third
+// of the LDS traffic of splitting the heads alone over the waves, and no V^T copy.
+//
+// Softmax reference: the softmax does not depend on it, so each head fixes it once, at the max of
+// the block's first tile, and the accumulators are never rescaled in the loop.  Later logits may
+// exceed it (weights above 1); if one exceeds it by more than 100 (log2 units, far from the fp32 and
+// bf16 overflow at 128) the block runs its tiles again with the observed maximum as reference.
+
+constexpr int kW32 = 4;                       // waves per block
+constexpr int kT32 = kW32 * kWave;
+constexpr int kH32 = 128;                     // heads per block
+constexpr int kPStride = kRowsPerTile + 8;    // bf16 per LDS P row (one head): 80 B
+constexpr int kDvPerWave = kDv / kW32;        // 128 value columns per wave in PV
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
+__device__ inline uint32_t pack_bf16x2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+}
+
+// 16 bytes per lane from global memory to LDS at lds_base + 16 * lane (lds_base wave-uniform), issued
+// as inline asm: the compiler then inserts no waits for it (it cannot tell which LDS reads the DMA may
+// overlap and would wait before every read of the other buffer); the kernel waits for it itself.
+__device__ inline void dma_row16(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const uint16_t *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane r names 4 consecutive bf16 at p; lane j
+// receives element j % 4 of the values named by lanes j / 4 + 4 i, i = 0 .. 3.
+__device__ inline u32x2 lds_read_tr16(const uint16_t *p)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4 *)(__attribute__((address_space(3))) uint16_t *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+__global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, const uint16_t *__restrict__ q,
+                                                               const uint16_t *__restrict__ kv, int n_heads,
+                                                               float scale, int k_sink, int k_swa, int k_sparse,
+                                                               const int32_t *__restrict__ idx,
+                                                               const int32_t *idx_row, int n_split,
+                                                               uint16_t *__restrict__ out, float *__restrict__ lse,
+                                                               AttnPartial part)
+{
+    const int split = blockIdx.x, r = blockIdx.y;
+    const int h_block = blockIdx.z * kH32;
+    // Two K tiles as distinct objects, each named statically below (the DMA into one does not make
+    // the compiler wait before reading the other), the P tile, the compacted picks.
+    __shared__ __attribute__((aligned(16))) uint16_t kt0[kDmaSlots * 8];
+    __shared__ __attribute__((aligned(16))) uint16_t kt1[kDmaSlots * 8];
+    __shared__ __attribute__((aligned(16))) uint16_t pt[kH32 * kPStride];
+    __shared__ int32_t sparse[kMaxSparse];
+    __shared__ int32_t scan_tmp[kT32 + 1 + kW32];
+    __shared__ int32_t tpos[2][kRowsPerTile];  // token positions of a tile's rows (-1: past the list)
+    __shared__ float head_m[kH32], head_l[kH32];
+
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges g = si_ranges(ri, k_sink, k_swa);
+    const int ir = idx_row ? idx_row[r] : r;
+    const bool ir_ok = ir >= 0 && ir < rows.n_rows;  // an index row outside idx contributes no picks
+    const int n_sp = compact_picks(idx + (int64_t)(ir_ok ? ir : 0) * k_sparse, ir_ok ? k_sparse : 0, g, sparse,
+                                   scan_tmp);
+    const SelList L = make_sel(ri, g, n_sp);
+
+    const int n_tiles = (L.total + kRowsPerTile - 1) / kRowsPerTile;
+    const int tiles_per_split = (n_tiles + n_split - 1) / n_split;
+    const int tile_lo = split * tiles_per_split;
+    const int tile_hi = min(tile_lo + tiles_per_split, n_tiles);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = lane_id();
+    const int n = lane & 31;   // QK: head 32 wave + n (B / C column) and K tile row (A row)
+    const int hh = lane >> 5;  // lane half
+
+    // Q^T B operands of the QK head: depth 16 ks + 8 hh .. +8, ks < 36.
+    u32x4 qb[36];
+    {
+        const uint16_t *qh = q + ((int64_t)r * n_heads + h_block + 32 * wave + n) * kDqk + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks)
+            qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 16 * ks);
+        // Complete the loads here: the compiler's own waits for them inside the tile loop would count
+        // the tile DMA too and stall on it.
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks)
+            asm volatile("" ::"v"(qb[ks]));
+    }
+    f32x16 o[16];  // index 4 mt + nt: O^T[dv 128 wave + 32 mt + 8 (i/4) + 4 hh + i%4][head 32 nt + n]
+    float m_ref = -INFINITY, m_obs = -INFINITY;  // QK head, log2 domain, scale folded in
+    float l_run = 0.0f;                          // QK head, this lane's rows
+    const float zs = scale * kLog2e;
+
+    auto tile_row_pos = [&](int tile, int row) -> int64_t {
+        const int j = tile * kRowsPerTile + row;
+        return j < L.total ? sel_pos(L, sparse, j) : -1;
+    };
+    // One tile = 32 rows x 73 16-byte slots (72 of data, one of padding against bank conflicts), moved
+    // by wave-wide 1 KB DMA writes: slot s of the tile receives chunk s % 73 of tile row s / 73.
+    // The rows' token positions come from the table tp (filled one tile ahead by 32 threads); padding
+    // slots and rows past the end of the list re-read an existing row of the sequence.
+    const uint16_t *kv_seq = kv + L.base * kDqk;
+    auto fill_table = [&](int tile, int32_t *tp) {
+        if (tid < kRowsPerTile)
+            tp[tid] = (int32_t)tile_row_pos(tile, tid);
+    };
+    auto issue_tile = [&](uint16_t *buf, const int32_t *tp) {
+        for (int jj = wave; jj < kDmaInstr; jj += kW32) {
+            const uint32_t slot = jj * kWave + lane;
+            const uint32_t row = (slot * 57457u) >> 22;  // slot / 73, exact for slot < 2368
+            const int chunk = (int)(slot - row * kSlotsPerRow);
+            const int32_t pos = tp[row < kRowsPerTile ? row : kRowsPerTile - 1];
+            const int cc = chunk < kChunksPerRow ? chunk : kChunksPerRow - 1;
+            const uint16_t *src = kv_seq + (int64_t)(pos >= 0 ? pos : 0) * kDqk + cc * 8;
+            dma_row16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + jj * kWave * 8)));
+        }
+    };
+
+    auto run_tile = [&](int tile, const uint16_t *ktc, uint16_t *ktn, int32_t *tpn) __attribute__((always_inline)) {
+        const bool more = tile + 1 < tile_hi;
+        if (more)
+            fill_table(tile + 1, tpn);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile has landed
+        __syncthreads();  // ... and every other wave's; PV of the last tile is done; next table written
+        if (more)
+            issue_tile(ktn, tpn);
+        // Rows past the end of the list occur in the list's last tile only.
+        const int n_valid = min(kRowsPerTile, L.total - tile * kRowsPerTile);
+        // QK: S^T[row 8 (i/4) + 4 hh + i%4][head n], i < 16.
+        f32x16 s = f32x16{};
+        {
+            const uint16_t *arow = ktc + n * kKStride + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(arow + 16 * ks);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                            __builtin_bit_cast(bf16x8, qb[ks]), s, 0, 0, 0);
+            }
+        }
+        float tmax = -INFINITY;
+        if (n_valid == kRowsPerTile) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s[i] *= zs;
+                tmax = fmaxf(tmax, s[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = 8 * (i >> 2) + 4 * hh + (i & 3);
+                s[i] = row < n_valid ? s[i] * zs : -INFINITY;
+                tmax = fmaxf(tmax, s[i]);
+            }
+        }
+        tmax = max_xor32(tmax);
+        if (m_ref == -INFINITY)
+            m_ref = tmax;  // the block's first tile (it always holds a row of the list)
+        m_obs = fmaxf(m_obs, tmax);
+        // P (bf16) to LDS as P[head][row]: lane (n, hh) holds rows 8 a + 4 hh .. +3 for a < 4.
+        uint16_t *prow = pt + (32 * wave + n) * kPStride + 4 * hh;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            float pv[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                pv[b] = __builtin_amdgcn_exp2f(s[4 * a + b] - m_ref);  // exp2(-inf) = 0; tiny weights flush to 0
+                l_run += pv[b];
+            }
+            *reinterpret_cast<u32x2 *>(prow + 8 * a) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        }
+        lds_barrier();  // P complete (the next tile's DMA keeps running)
+        // PV: 4 dv tiles x 4 head tiles x 2 row steps of 16.
+        const int j16 = lane & 15, g16 = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 av[4], bv[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                // lane (g16, j16) names rows 16 ks + 8 (g16 / 2) + 4 t + j16 / 4, columns
+                // dv0 + 4 (j16 % 4) .. +3: it then holds V[16 ks + 8 hh + 0 .. 7][dv0 + j16], the A
+                // operand V^T[dv][row] of its lane.
+                const int dv0 = kDvPerWave * wave + 32 * mt + 16 * (g16 & 1);
+                const uint16_t *vp = ktc + (16 * ks + 8 * (g16 >> 1) + (j16 >> 2)) * kKStride + dv0 + 4 * (j16 & 3);
+                const u32x2 lo = lds_read_tr16(vp), hi = lds_read_tr16(vp + 4 * kKStride);
+                av[mt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                bv[nt] = *reinterpret_cast<const u32x4 *>(pt + (32 * nt + n) * kPStride + 16 * ks + 8 * hh);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    o[4 * mt + nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, av[mt]), __builtin_bit_cast(bf16x8, bv[nt]), o[4 * mt + nt], 0, 0,
+                        0);
+        }
+    };
+
+    for (int sweep = 0; sweep < 2; ++sweep) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            o[i] = f32x16{};
+        l_run = 0.0f;
+        if (tile_lo < tile_hi) {
+            fill_table(tile_lo, tpos[tile_lo & 1]);
+            __syncthreads();
+            issue_tile((tile_lo & 1) ? kt1 : kt0, tpos[tile_lo & 1]);
+        }
+        int tile = tile_lo;
+        if (tile < tile_hi && (tile & 1)) {
+            run_tile(tile, kt1, kt0, tpos[0]);
+            ++tile;
+        }
+        for (; tile < tile_hi; tile += 2) {
+            run_tile(tile, kt0, kt1, tpos[1]);
+            if (tile + 1 < tile_hi)
+                run_tile(tile + 1, kt1, kt0, tpos[0]);
+        }
+        // Run again only if some head's logits outgrew its reference by the overflow margin.
+        if (!__syncthreads_or(m_obs > m_ref + 100.0f))
+            break;
+        m_ref = m_obs;
+    }
+
+    // Per-head reference and sum from the QK waves, for the value columns of every wave.
+    const float l_tot = sum_xor32(l_run);
+    if (hh == 0) {
+        head_m[32 * wave + n] = m_ref;
+        head_l[32 * wave + n] = l_tot;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int hl = 32 * nt + n, head = h_block + hl;
+        const float mh = head_m[hl], lh = head_l[hl];
+        if (n_split == 1) {
+            const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
+            uint16_t *oh = out + ((int64_t)r * n_heads + head) * kDv + kDvPerWave * wave;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x16 &acc = o[4 * mt + nt];
+                    *reinterpret_cast<u32x2 *>(oh + 32 * mt + 8 * i4 + 4 * hh) =
+                        u32x2{pack_bf16x2(acc[4 * i4] * inv, acc[4 * i4 + 1] * inv),
+                              pack_bf16x2(acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv)};
+                }
+            if (lse && wave == 0 && hh == 0)
+                lse[(int64_t)r * n_heads + head] = lh > 0.0f ? (mh + log2f(lh)) / kLog2e : -INFINITY;
+        } else {
+            const int64_t slot = ((int64_t)r * n_split + split) * n_heads + head;
+            float *oh = part.o + slot * kDv + kDvPerWave * wave;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x16 &acc = o[4 * mt + nt];
+                    *reinterpret_cast<f32x4 *>(oh + 32 * mt + 8 * i4 + 4 * hh) =
+                        f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+                }
+            if (wave == 0 && hh == 0) {
+                part.m[slot] = mh;
+                part.l[slot] = lh;
+            }
+        }
+    }
+}
+
 // Combines the split partials of one (row, head): the same rescaling rule as inside the kernel.
 __global__ __launch_bounds__(256) void attn_merge_kernel(int n_heads, int n_split, AttnPartial part,
                                                           uint16_t *__restrict__ out, float *__restrict__ lse)
@@ -519,8 +811,14 @@ hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, con
         part.l = (float *)p;
     }
     dim3 grid(ns, rows.n_rows, (n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
-    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kAttnThreads), 0, stream, rows, (const uint16_t *)q, (const uint16_t *)kv,
-                       n_heads, scale, k_sink, k_swa, k_sparse, idx, idx_row, ns, (uint16_t *)out, lse, part);
+    if (n_heads % kH32 == 0)
+        hipLaunchKernelGGL(attn_mfma32_kernel, grid, dim3(kT32), 0, stream, rows, (const uint16_t *)q,
+                           (const uint16_t *)kv, n_heads, scale, k_sink, k_swa, k_sparse, idx, idx_row, ns,
+                           (uint16_t *)out, lse, part);
+    else
+        hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(kAttnThreads), 0, stream, rows, (const uint16_t *)q,
+                           (const uint16_t *)kv, n_heads, scale, k_sink, k_swa, k_sparse, idx, idx_row, ns,
+                           (uint16_t *)out, lse, part);
     if (ns > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3(rows.n_rows, n_heads), dim3(256), 0, stream, n_heads, ns, part,
                            (uint16_t *)out, lse);

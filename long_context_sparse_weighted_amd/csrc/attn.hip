@@ -212,9 +212,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(RowsDev rows, const floa
 __device__ inline int vt_row(int c) { return 16 * ((c >> 2) & 1) + 4 * (c >> 3) + (c & 3); }
 
 struct AttnPartial {
-    float *o;  // [n_rows][n_split][n_heads][kDv] unnormalised
-    float *m;  // [n_rows][n_split][n_heads] reference max (log2 domain, scale folded in)
-    float *l;  // [n_rows][n_split][n_heads]
+    uint16_t *o;  // [n_rows][n_split][n_heads][kDv] bf16, normalised by the split's own l
+    float *m;     // [n_rows][n_split][n_heads] reference max (log2 domain, scale folded in)
+    float *l;     // [n_rows][n_split][n_heads] sum of the split's weights against m
 };
 
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows, const uint16_t *__restrict__ q,
@@ -415,10 +415,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_mfma_kernel(RowsDev rows
             lse[(int64_t)r * n_heads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) / kLog2e : -INFINITY;
     } else {
         const int64_t slot = ((int64_t)r * n_split + split) * n_heads + head;
-        float *oh = part.o + slot * kDv;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint16_t *oh = part.o + slot * kDv;
 #pragma unroll
-        for (int mt = 0; mt < 32; ++mt)
-            *reinterpret_cast<f32x4 *>(&oh[mt * 16 + 4 * gq]) = o[mt];
+        for (int mt = 0; mt < 32; ++mt) {
+            uint32_t w0 = (uint32_t)float_to_bf16_bits(o[mt][0] * inv) | ((uint32_t)float_to_bf16_bits(o[mt][1] * inv) << 16);
+            uint32_t w1 = (uint32_t)float_to_bf16_bits(o[mt][2] * inv) | ((uint32_t)float_to_bf16_bits(o[mt][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(&oh[mt * 16 + 4 * gq]) = make_uint2(w0, w1);
+        }
         if (gq == 0) {
             part.m[slot] = m_run;
             part.l[slot] = l_tot;
@@ -555,26 +559,38 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
         if (tid < kRowsPerTile)
             tp[tid] = (int32_t)tile_row_pos(tile, tid);
     };
-    auto issue_tile = [&](uint16_t *buf, const int32_t *tp) {
-        for (int jj = wave; jj < kDmaInstr; jj += kW32) {
-            const uint32_t slot = jj * kWave + lane;
+    constexpr int kDmaPerWave = (kDmaInstr + kW32 - 1) / kW32;
+    // Wave w moves DMA writes w, w + 4, ... of a tile, either back to back or spread over the QK
+    // products of the current tile.  lane_v is the lane index through an opaque copy, taken once per
+    // tile: the per-lane offsets are then derived anew for each tile instead of being kept live (and
+    // spilled) across the tile loop.
+    auto opaque_lane = [&]() __attribute__((always_inline)) {
+        uint32_t v;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "v"(lane));
+        return v;
+    };
+    auto issue_one = [&](int t, uint16_t *buf, const int32_t *tp) __attribute__((always_inline)) {
+        const int jj = wave + kW32 * t;
+        if (jj < kDmaInstr) {
+            const uint32_t lane_v = opaque_lane();  // keeps this address math next to its DMA
+            const uint32_t slot = jj * kWave + lane_v;
             const uint32_t row = (slot * 57457u) >> 22;  // slot / 73, exact for slot < 2368
-            const int chunk = (int)(slot - row * kSlotsPerRow);
             const int32_t pos = tp[row < kRowsPerTile ? row : kRowsPerTile - 1];
+            const int chunk = (int)(slot - row * kSlotsPerRow);
             const int cc = chunk < kChunksPerRow ? chunk : kChunksPerRow - 1;
-            const uint16_t *src = kv_seq + (int64_t)(pos >= 0 ? pos : 0) * kDqk + cc * 8;
+            const uint16_t *src = kv_seq + (int64_t)max(pos, 0) * kDqk + cc * 8;
             dma_row16(src, __builtin_amdgcn_readfirstlane(lds_addr(buf + jj * kWave * 8)));
         }
     };
+    auto issue_tile = [&](uint16_t *buf, const int32_t *tp) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < kDmaPerWave; ++t)
+            issue_one(t, buf, tp);
+    };
 
-    auto run_tile = [&](int tile, const uint16_t *ktc, uint16_t *ktn, int32_t *tpn) __attribute__((always_inline)) {
-        const bool more = tile + 1 < tile_hi;
-        if (more)
-            fill_table(tile + 1, tpn);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile has landed
-        __syncthreads();  // ... and every other wave's; PV of the last tile is done; next table written
-        if (more)
-            issue_tile(ktn, tpn);
+    // One tile; when MORE, the next tile's DMA writes are interleaved with its products.
+    auto tile_body = [&](bool more, int tile, const uint16_t *ktc, uint16_t *ktn, const int32_t *tpn)
+                         __attribute__((always_inline)) {
         // Rows past the end of the list occur in the list's last tile only.
         const int n_valid = min(kRowsPerTile, L.total - tile * kRowsPerTile);
         // QK: S^T[row 8 (i/4) + 4 hh + i%4][head n], i < 16.
@@ -586,6 +602,10 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
                 const u32x4 a = *reinterpret_cast<const u32x4 *>(arow + 16 * ks);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                             __builtin_bit_cast(bf16x8, qb[ks]), s, 0, 0, 0);
+                // Each DMA write stalls this wave's instruction issue for ~100+ cycles: writes 0 .. 4 of
+                // the next tile are spread over the QK products, 5 .. 9 over the PV products.
+                if (ks % 7 == 3 && more)
+                    issue_one(ks / 7, ktn, tpn);
             }
         }
         float tmax = -INFINITY;
@@ -641,11 +661,23 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+                for (int nt = 0; nt < 4; ++nt) {
                     o[4 * mt + nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, av[mt]), __builtin_bit_cast(bf16x8, bv[nt]), o[4 * mt + nt], 0, 0,
                         0);
+                    const int m = 16 * ks + 4 * mt + nt;
+                    if (m % 6 == 3 && m / 6 < kDmaPerWave - 5 && more)
+                        issue_one(5 + m / 6, ktn, tpn);
+                }
         }
+    };
+    auto run_tile = [&](int tile, const uint16_t *ktc, uint16_t *ktn, int32_t *tpn) __attribute__((always_inline)) {
+        const bool more = tile + 1 < tile_hi;
+        if (more)
+            fill_table(tile + 1, tpn);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of the tile has landed
+        __syncthreads();  // ... and every other wave's; PV of the last tile is done; next table written
+        tile_body(more, tile, ktc, ktn, tpn);
     };
 
     for (int sweep = 0; sweep < 2; ++sweep) {
@@ -681,36 +713,44 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
         head_l[32 * wave + n] = l_tot;
     }
     __syncthreads();
+    // O (normalised, bf16) of the block's 128 heads: the final output, or this split's partial.  Each
+    // wave stages 32 heads x its 128 value columns in LDS (the first K tile is free now) and writes
+    // them back as whole 256-byte runs of head rows.
+    uint16_t *dst = n_split == 1 ? out + ((int64_t)r * n_heads + h_block) * kDv
+                                 : part.o + (((int64_t)r * n_split + split) * n_heads + h_block) * kDv;
+    constexpr int kStg = kDvPerWave + 8;  // bf16 per staged head row (272 B: rows on different banks)
+    uint16_t *stg = kt0 + wave * 32 * kStg;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-        const int hl = 32 * nt + n, head = h_block + hl;
-        const float mh = head_m[hl], lh = head_l[hl];
-        if (n_split == 1) {
-            const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
-            uint16_t *oh = out + ((int64_t)r * n_heads + head) * kDv + kDvPerWave * wave;
+        const float lh = head_l[32 * nt + n];
+        const float inv = lh > 0.0f ? 1.0f / lh : 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x16 &acc = o[4 * mt + nt];
-                    *reinterpret_cast<u32x2 *>(oh + 32 * mt + 8 * i4 + 4 * hh) =
-                        u32x2{pack_bf16x2(acc[4 * i4] * inv, acc[4 * i4 + 1] * inv),
-                              pack_bf16x2(acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv)};
-                }
-            if (lse && wave == 0 && hh == 0)
-                lse[(int64_t)r * n_heads + head] = lh > 0.0f ? (mh + log2f(lh)) / kLog2e : -INFINITY;
-        } else {
-            const int64_t slot = ((int64_t)r * n_split + split) * n_heads + head;
-            float *oh = part.o + slot * kDv + kDvPerWave * wave;
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const f32x16 &acc = o[4 * mt + nt];
+                *reinterpret_cast<u32x2 *>(stg + n * kStg + 32 * mt + 8 * i4 + 4 * hh) =
+                    u32x2{pack_bf16x2(acc[4 * i4] * inv, acc[4 * i4 + 1] * inv),
+                          pack_bf16x2(acc[4 * i4 + 2] * inv, acc[4 * i4 + 3] * inv)};
+            }
+        // The wave reads back only what its own lanes wrote (a wave's LDS operations complete in order).
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+        for (int it = 0; it < 8; ++it) {
+            const int hrow = 4 * it + (lane >> 4), ch = lane & 15;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + hrow * kStg + 8 * ch);
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)(32 * nt + hrow) * kDv + kDvPerWave * wave + 8 * ch) = v;
+        }
+    }
+    if (wave == 0 && hh == 0) {
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x16 &acc = o[4 * mt + nt];
-                    *reinterpret_cast<f32x4 *>(oh + 32 * mt + 8 * i4 + 4 * hh) =
-                        f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
-                }
-            if (wave == 0 && hh == 0) {
+        for (int nt = 0; nt < 4; ++nt) {
+            const int hl = 32 * nt + n, head = h_block + hl;
+            const float mh = head_m[hl], lh = head_l[hl];
+            if (n_split == 1) {
+                if (lse)
+                    lse[(int64_t)r * n_heads + head] = lh > 0.0f ? (mh + log2f(lh)) / kLog2e : -INFINITY;
+            } else {
+                const int64_t slot = ((int64_t)r * n_split + split) * n_heads + head;
                 part.m[slot] = mh;
                 part.l[slot] = lh;
             }
@@ -718,35 +758,49 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
     }
 }
 
-// Combines the split partials of one (row, head): the same rescaling rule as inside the kernel.
+// Combines the split partials of one (row, head) (one wave per head; lane l owns value columns
+// 8 l .. 8 l + 7): split s enters with weight l_s 2^(m_s - M), M the largest m_s.
 __global__ __launch_bounds__(256) void attn_merge_kernel(int n_heads, int n_split, AttnPartial part,
                                                           uint16_t *__restrict__ out, float *__restrict__ lse)
 {
-    const int r = blockIdx.x, h = blockIdx.y;
-    __shared__ float wsp[kMaxSplitMerge];
-    float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s)
-        mx = fmaxf(mx, part.m[((int64_t)r * n_split + s) * n_heads + h]);
-    float l = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-        int64_t slot = ((int64_t)r * n_split + s) * n_heads + h;
-        float ms = part.m[slot];
-        float wgt = ms == -INFINITY ? 0.0f : exp2f(ms - mx);
-        if (threadIdx.x == 0)
-            wsp[s] = wgt;
-        l += wgt * part.l[slot];
+    const int r = blockIdx.x;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (h >= n_heads)
+        return;
+    const int lane = lane_id();
+    const int64_t slot0 = (int64_t)r * n_split * n_heads + h;  // split s at slot0 + s n_heads
+    float ms = -INFINITY, ls = 0.0f;
+    if (lane < n_split) {
+        ms = part.m[slot0 + (int64_t)lane * n_heads];
+        ls = part.l[slot0 + (int64_t)lane * n_heads];
     }
-    __syncthreads();
+    const float mx = wave_max(ms);
+    const float w = ls > 0.0f ? ls * exp2f(ms - mx) : 0.0f;
+    const float l = wave_sum(w);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < n_split; s0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int sp = min(s0 + k, n_split - 1);
+            v[k] = *reinterpret_cast<const u32x4 *>(part.o + (slot0 + (int64_t)sp * n_heads) * kDv + 8 * lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), min(s0 + k, kWave - 1)));
+            const float wt = s0 + k < n_split ? wk : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += wt * __uint_as_float(v[k][i] << 16);
+                acc[2 * i + 1] += wt * __uint_as_float(v[k][i] & 0xffff0000u);
+            }
+        }
+    }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    uint16_t *oh = out + ((int64_t)r * n_heads + h) * kDv;
-    for (int d = threadIdx.x; d < kDv; d += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < n_split; ++s)
-            if (wsp[s] != 0.0f)
-                acc += wsp[s] * part.o[(((int64_t)r * n_split + s) * n_heads + h) * kDv + d];
-        oh[d] = float_to_bf16_bits(acc * inv);
-    }
-    if (lse && threadIdx.x == 0)
+    *reinterpret_cast<u32x4 *>(out + ((int64_t)r * n_heads + h) * kDv + 8 * lane) =
+        u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+    if (lse && lane == 0)
         lse[(int64_t)r * n_heads + h] = l > 0.0f ? (mx + log2f(l)) / kLog2e : -INFINITY;
 }
 
@@ -774,7 +828,7 @@ size_t attn_workspace_bytes(int dtype, int n_rows, int n_heads, int d_v, int k_t
     if (ns == 1)
         return 0;
     size_t slots = (size_t)n_rows * ns * n_heads;
-    return align_up(slots * kDv * sizeof(float)) + 2 * align_up(slots * sizeof(float));
+    return align_up(slots * kDv * sizeof(uint16_t)) + 2 * align_up(slots * sizeof(float));
 }
 
 bool attn_supported(int dtype, int n_heads, int d_qk, int d_v, int k_sparse, int k_total)
@@ -804,8 +858,8 @@ hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, con
     if (ns > 1) {
         size_t slots = (size_t)rows.n_rows * ns * n_heads;
         char *p = (char *)ws;
-        part.o = (float *)p;
-        p += align_up(slots * kDv * sizeof(float));
+        part.o = (uint16_t *)p;
+        p += align_up(slots * kDv * sizeof(uint16_t));
         part.m = (float *)p;
         p += align_up(slots * sizeof(float));
         part.l = (float *)p;
@@ -820,7 +874,7 @@ hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, con
                            (const uint16_t *)kv, n_heads, scale, k_sink, k_swa, k_sparse, idx, idx_row, ns,
                            (uint16_t *)out, lse, part);
     if (ns > 1)
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(rows.n_rows, n_heads), dim3(256), 0, stream, n_heads, ns, part,
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(rows.n_rows, (n_heads + 3) / 4), dim3(256), 0, stream, n_heads, ns, part,
                            (uint16_t *)out, lse);
     return hipGetLastError();
 }

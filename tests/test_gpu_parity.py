@@ -275,6 +275,20 @@ def test_attention_bf16_vs_oracle(budget):
     assert np.all(f64(host(out))[-1] == 0) and np.all(np.isneginf(host(lse)[-1]))
 
 
+@pytest.mark.parametrize("heads", [16, 48, 256])
+def test_attention_bf16_head_counts(heads):
+    # 16 and 48 heads take the 16-heads-per-wave kernel, 256 two blocks of the 128-head kernel
+    x = custom_rows(RAGGED_LENGTHS, RAGGED_ROWS, H=heads, seed=23)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx = _oracle_idx_for(x, c["k_sparse"], np.random.default_rng(4))
+    out, lse = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], budget_of(c),
+                                   torch.from_numpy(idx).to(DEV))
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], o["row_seq"], o["row_pos"], o["q"], o["kv"], 512, c["scale"],
+                                     c["k_sink"], c["k_swa"], idx)
+    log(f"bf16 attn H={heads} max err", assert_attn_close(host(out), want_o, host(lse), want_l, 2e-2))
+
+
 def test_attention_bf16_many_rows_single_split():
     # enough rows that each row runs in one block (no split partials)
     lengths = [3000] * 4

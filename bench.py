@@ -288,6 +288,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--lengths", default="131072,1048576")
+    ap.add_argument("--hi-lengths", default="262144,524288,1048576", help="KV lengths of the HI workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="decode", choices=["decode", "hi", "prefill", "ragged", "tiny", "all"],
                     help="decode prints the metric line; the others print their own figures as one JSON line")
@@ -304,7 +305,8 @@ def main():
     if args.workload != "decode":
         extra = {}
         if args.workload in ("hi", "all"):
-            extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup)
+            extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup,
+                                                 lengths=[int(v) for v in args.hi_lengths.split(",")])
         if args.workload in ("prefill", "all"):
             extra["chunked_prefill_cli"] = bench_prefill(args.steps, args.warmup)
         if args.workload in ("ragged", "all"):

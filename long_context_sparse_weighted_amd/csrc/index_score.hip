@@ -770,7 +770,7 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
     return n_heads >= 1 && n_heads <= kHeads && (head_dim == 64 || head_dim == 128);
 }
 
-// Columns per block of the bf16 kernels: enough blocks to cover the chip a few times over.
+// Columns per block of the bf16 kernels: about one block per CU (256 CUs), at most 16384 columns.
 struct ScoreGeom {
     int64_t chunk_elems;
     int n_chunks;
@@ -778,7 +778,7 @@ struct ScoreGeom {
 
 static ScoreGeom score_geometry(int64_t n_rows, int64_t n_cols)
 {
-    int64_t cpb = n_rows * n_cols / 2048;
+    int64_t cpb = n_rows * n_cols / 256;  // large blocks amortise the ring ramp-up and the Q / w loads
     cpb = (cpb + 63) / 64 * 64;
     if (cpb < 256)
         cpb = 256;

@@ -104,12 +104,13 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
         // keys whose top `consumed` bits equal the prefix: (x & pmask) == pval (uniform scalars)
         const uint32_t pmask = sel.consumed == 0 ? 0u : ~0u << (32 - sel.consumed);
         const uint32_t pval = sel.consumed == 0 ? 0u : sel.prefix << (32 - sel.consumed);
-        // (Key 0, not a candidate, falls in pass-0 bin 0, below every candidate key: a digit
-        // below 3 is never selected while there are more than k candidates.)
+        // Key 0 (not a candidate) is not counted: it goes to the dummy word like the keys outside the
+        // prefix (segments padded with zeros would otherwise pile their atomics onto bin 0).  No
+        // candidate key falls in pass-0 bin 0 (its top 11 bits would make it -inf or a NaN).
 #pragma unroll
         for (int m = 0; m < kVpt; ++m) {
             const uint32_t x = key[m];
-            const bool take = (x & pmask) == pval;
+            const bool take = (x & pmask) == pval && x != 0u;
             atomicAdd(&hist[take ? kCopies * ((x >> shift) & dmask) + copy : dummy], 1u);
         }
         __syncthreads();
@@ -182,6 +183,26 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
     } else {
         t_gt = sel.prefix + 1u, t_eq = sel.prefix;  // consumed == 32: prefix is T
     }
+    const uint32_t dummy = kMaxLocalK + (uint32_t)lane_id();
+    if (t_eq == 0xffffffffu) {
+        // No ties to resolve (the usual case: the threshold bin was taken whole): the picks are the
+        // keys >= t_gt, numbered in position order.
+        uint32_t cg = 0;
+#pragma unroll
+        for (int m = 0; m < kVpt; ++m)
+            cg += key[m] >= t_gt ? 1u : 0u;
+        uint32_t bg, unused, tg, unused2;
+        block_scan2<NT>(cg, 0, bg, unused, tg, unused2, scratch);
+#pragma unroll
+        for (int m = 0; m < kVpt; ++m) {
+            const bool g = key[m] >= t_gt;
+            const uint32_t slot = g ? bg : dummy;
+            stage_key[slot] = key[m];
+            stage_li[slot] = first_li + m;
+            bg += g ? 1u : 0u;
+        }
+        return tg;
+    }
     // Flags of this thread's keys as bit masks (bit m: key m).
     uint64_t gbits = 0, ebits = 0;
 #pragma unroll
@@ -192,7 +213,6 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
     const uint32_t cg = (uint32_t)__popcll(gbits), ce = (uint32_t)__popcll(ebits);
     uint32_t bg, be, tg, te;
     block_scan2<NT>(cg, ce, bg, be, tg, te, scratch);
-    const uint32_t dummy = kMaxLocalK + (uint32_t)lane_id();
 #pragma unroll
     for (int m = 0; m < kVpt; ++m) {
         const bool g = (gbits >> m) & 1u, e = (ebits >> m) & 1u;
@@ -239,6 +259,26 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
 #pragma unroll
             for (int q = 0; q < kVpt / 4; ++q) {
                 const float4 v = src[q];
+                key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
+                key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
+                key[4 * q + 2] = is_candidate(v.z) ? float_order_key(v.z) : 0u;
+                key[4 * q + 3] = is_candidate(v.w) ? float_order_key(v.w) : 0u;
+            }
+        } else if ((ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
+            // A partial segment: whole float4 where it lies below n_in, single elements only in the
+            // float4 that straddles it.
+            const float4 *src = reinterpret_cast<const float4 *>(row + base);
+#pragma unroll
+            for (int q = 0; q < kVpt / 4; ++q) {
+                const int64_t c = base + 4 * q;
+                float4 v = float4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                if (c + 4 <= n_in) {
+                    v = src[q];
+                } else if (c < n_in) {
+                    v.x = row[c];
+                    v.y = c + 1 < n_in ? row[c + 1] : -INFINITY;
+                    v.z = c + 2 < n_in ? row[c + 2] : -INFINITY;
+                }
                 key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
                 key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
                 key[4 * q + 2] = is_candidate(v.z) ? float_order_key(v.z) : 0u;

@@ -451,16 +451,21 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
     const lsa_budget_t bud = cfg->budget;
     hipError_t e = hipSuccess;
     if (owner && rows->n_rows > 0) {
-        e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
+        // Row roles are only needed when some row can differ: with neither HI nor shared index rows
+        // every row runs the flat indexer and the kernels run ungated.
+        const bool need_modes = use_hi || idx_row != nullptr;
+        if (need_modes)
+            e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
+        const uint8_t *flat_gate = need_modes ? lw.row_mode : nullptr;
         const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
         // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
         if (e == hipSuccess)
             e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                    cfg->head_dim_idx, bud.k_sink, bud.k_swa, nullptr, 0, 1, lw.flat_scores, ld,
-                                   RowGate{lw.row_mode, 1}, stream);
+                                   RowGate{flat_gate, 1}, stream);
         if (e == hipSuccess)
             e = launch_topk(rows->n_rows, lw.flat_scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, lw.topk_ws,
-                            RowGate{lw.row_mode, 1}, stream);
+                            RowGate{flat_gate, 1}, stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);

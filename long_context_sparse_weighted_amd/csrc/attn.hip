@@ -509,6 +509,22 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
     __shared__ int32_t tpos[2][kRowsPerTile];  // token positions of a tile's rows (-1: past the list)
     __shared__ float head_m[kH32], head_l[kH32];
 
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = lane_id();
+    const int n = lane & 31;   // QK: head 32 wave + n (B / C column) and K tile row (A row)
+    const int hh = lane >> 5;  // lane half
+
+    // Q^T B operands of the QK head: depth 16 ks + 8 hh .. +8, ks < 36.  Issued first: their latency
+    // overlaps the reads of the row descriptor and of the picks below.
+    u32x4 qb[36];
+    {
+        const uint16_t *qh = q + ((int64_t)r * n_heads + h_block + 32 * wave + n) * kDqk + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks)
+            qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 16 * ks);
+    }
+
     const RowInfo ri = row_info(rows, r);
     const SiRanges g = si_ranges(ri, k_sink, k_swa);
     const int ir = idx_row ? idx_row[r] : r;
@@ -522,25 +538,11 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
     const int tile_lo = split * tiles_per_split;
     const int tile_hi = min(tile_lo + tiles_per_split, n_tiles);
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = lane_id();
-    const int n = lane & 31;   // QK: head 32 wave + n (B / C column) and K tile row (A row)
-    const int hh = lane >> 5;  // lane half
-
-    // Q^T B operands of the QK head: depth 16 ks + 8 hh .. +8, ks < 36.
-    u32x4 qb[36];
-    {
-        const uint16_t *qh = q + ((int64_t)r * n_heads + h_block + 32 * wave + n) * kDqk + 8 * hh;
+    // Complete the Q loads here: the compiler's own waits for them inside the tile loop would count
+    // the tile DMA too and stall on it.
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks)
-            qb[ks] = *reinterpret_cast<const u32x4 *>(qh + 16 * ks);
-        // Complete the loads here: the compiler's own waits for them inside the tile loop would count
-        // the tile DMA too and stall on it.
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks)
-            asm volatile("" ::"v"(qb[ks]));
-    }
+    for (int ks = 0; ks < 36; ++ks)
+        asm volatile("" ::"v"(qb[ks]));
     f32x16 o[16];  // index 4 mt + nt: O^T[dv 128 wave + 32 mt + 8 (i/4) + 4 hh + i%4][head 32 nt + n]
     float m_ref = -INFINITY, m_obs = -INFINITY;  // QK head, log2 domain, scale folded in
     float l_run = 0.0f;                          // QK head, this lane's rows

@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 // outstanding" stricter.
 
 #ifndef LSA_SCORE_RING
-#define LSA_SCORE_RING 4
+#define LSA_SCORE_RING 6
 #endif
 constexpr int kScoreRing = LSA_SCORE_RING;
 

@@ -157,7 +157,7 @@ def time_layer(x, cfg, steps, warmup, idx_row=None, sb_off=None, k_mean=None, q=
     import torch
 
     import long_context_sparse_weighted_amd as lsa
-    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"])
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"], min(x["lengths"]))
     n = x["row_pos"].numel()
     layer = lsa.Layer(cfg, rows, torch.bfloat16, "cuda", use_hi=k_mean is not None)
     if idx is None:

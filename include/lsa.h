@@ -57,6 +57,9 @@ typedef struct lsa_rows {
     const int32_t *row_seq;  /* device [n_rows]: sequence of each row, in [0, n_seq) */
     const int32_t *row_pos;  /* device [n_rows]: position t of each row */
     int64_t max_kv_len;      /* host: an upper bound of every L_b; sizes grids and buffers */
+    int64_t min_kv_len;      /* host: a lower bound of every L_b, or 0 when not known (0 <= min <= max);
+                                used only to skip passes no row needs (lsa_layer_fwd: with
+                                min_kv_len >= hi_min_len no row runs the flat indexer) */
 } lsa_rows_t;
 
 /* SI budget: K = k_sink + k_swa + k_sparse (the pages use 16 + 1024 + 1024, [paper] §3.1). */

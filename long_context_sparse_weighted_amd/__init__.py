@@ -30,7 +30,8 @@ class LsaError(RuntimeError):
 
 class Rows(ctypes.Structure):
     _fields_ = [("n_seq", ctypes.c_int32), ("n_rows", ctypes.c_int32), ("kv_off", ctypes.c_void_p),
-                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p), ("max_kv_len", ctypes.c_int64)]
+                ("row_seq", ctypes.c_void_p), ("row_pos", ctypes.c_void_p), ("max_kv_len", ctypes.c_int64),
+                ("min_kv_len", ctypes.c_int64)]
 
 
 class Budget(ctypes.Structure):
@@ -108,18 +109,20 @@ def _need(t, dtype, name):
 
 @dataclass
 class RowsDesc:
-    """Rows of a batch: device tensors kv_off (int64 [n_seq+1]), row_seq / row_pos (int32 [n_rows])."""
+    """Rows of a batch: device tensors kv_off (int64 [n_seq+1]), row_seq / row_pos (int32 [n_rows]);
+    max_kv_len bounds every sequence length from above, min_kv_len (0: not known) from below."""
     kv_off: torch.Tensor
     row_seq: torch.Tensor
     row_pos: torch.Tensor
     max_kv_len: int
+    min_kv_len: int = 0
 
     def c(self):
         _need(self.kv_off, torch.int64, "kv_off")
         _need(self.row_seq, torch.int32, "row_seq")
         _need(self.row_pos, torch.int32, "row_pos")
         return Rows(self.kv_off.numel() - 1, self.row_pos.numel(), _p(self.kv_off), _p(self.row_seq),
-                    _p(self.row_pos), int(self.max_kv_len))
+                    _p(self.row_pos), int(self.max_kv_len), int(self.min_kv_len))
 
 
 def _workspace(nbytes, device):

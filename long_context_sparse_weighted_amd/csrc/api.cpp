@@ -51,6 +51,8 @@ int check_rows(const lsa_rows_t *rows)
         return fail(LSA_ERR_INVALID, "rows: kv_off / row_seq / row_pos must be device pointers");
     if (rows->n_rows > kMaxGridRows)
         return fail(LSA_ERR_UNSUPPORTED, "n_rows %d exceeds %lld", rows->n_rows, (long long)kMaxGridRows);
+    if (rows->min_kv_len < 0 || rows->min_kv_len > rows->max_kv_len)
+        return fail(LSA_ERR_INVALID, "min_kv_len must lie in [0, max_kv_len]");
     if (rows->max_kv_len >= (int64_t)1 << 31)
         return fail(LSA_ERR_UNSUPPORTED, "max_kv_len must be below 2^31");
     return LSA_OK;
@@ -451,21 +453,23 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
     const lsa_budget_t bud = cfg->budget;
     hipError_t e = hipSuccess;
     if (owner && rows->n_rows > 0) {
-        // Row roles are only needed when some row can differ: with neither HI nor shared index rows
-        // every row runs the flat indexer and the kernels run ungated.
-        const bool need_modes = use_hi || idx_row != nullptr;
+        // Row roles are only needed when rows can differ: with neither shared index rows nor a mix of
+        // flat and HI rows (no HI, or every sequence at least hi_min_len long) the kernels run ungated,
+        // and when every row takes HI the flat passes are not launched.
+        const bool all_hi = use_hi && rows->min_kv_len >= cfg->hi_min_len;
+        const bool need_modes = (use_hi && !all_hi) || idx_row != nullptr;
         if (need_modes)
             e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
-        const uint8_t *flat_gate = need_modes ? lw.row_mode : nullptr;
+        const uint8_t *gate = need_modes ? lw.row_mode : nullptr;
         const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
         // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
-        if (e == hipSuccess)
+        if (e == hipSuccess && !all_hi)
             e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                    cfg->head_dim_idx, bud.k_sink, bud.k_swa, nullptr, 0, 1, lw.flat_scores, ld,
-                                   RowGate{flat_gate, 1}, stream);
-        if (e == hipSuccess)
+                                   RowGate{gate, 1}, stream);
+        if (e == hipSuccess && !all_hi)
             e = launch_topk(rows->n_rows, lw.flat_scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, lw.topk_ws,
-                            RowGate{flat_gate, 1}, stream);
+                            RowGate{gate, 1}, stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);
@@ -473,17 +477,17 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
             if (e == hipSuccess)
                 e = launch_page_scores(cfg->dtype, rd, rows->max_kv_len, sb_off, q_idx, w, k_mean, cfg->n_heads_idx,
                                        cfg->head_dim_idx, cfg->P, cfg->B, lw.page_scores, n_pages,
-                                       RowGate{lw.row_mode, 2}, stream);
+                                       RowGate{gate, 2}, stream);
             if (e == hipSuccess)
                 e = launch_topk(rows->n_rows, lw.page_scores, n_pages, n_pages, nullptr, 0, 1, cfg->M, lw.pages,
-                                lw.page_topk_ws, RowGate{lw.row_mode, 2}, stream);
+                                lw.page_topk_ws, RowGate{gate, 2}, stream);
             if (e == hipSuccess)
                 e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                        cfg->head_dim_idx, bud.k_sink, bud.k_swa, lw.pages, cfg->M, cfg->P,
-                                       lw.comp_scores, n_comp, RowGate{lw.row_mode, 2}, stream);
+                                       lw.comp_scores, n_comp, RowGate{gate, 2}, stream);
             if (e == hipSuccess)
                 e = launch_topk(rows->n_rows, lw.comp_scores, n_comp, n_comp, lw.pages, cfg->M, cfg->P, bud.k_sparse,
-                                idx, lw.topk_ws, RowGate{lw.row_mode, 2}, stream);
+                                idx, lw.topk_ws, RowGate{gate, 2}, stream);
         }
     }
     if (e == hipSuccess)

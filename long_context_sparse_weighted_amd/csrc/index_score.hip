@@ -340,16 +340,26 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     const int n = lane & 15;
     const int g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
-    const int64_t c_begin = (int64_t)blockIdx.x * cols_per_block;
-    const int64_t c_end = c_begin + cols_per_block < n_cols ? c_begin + cols_per_block : n_cols;
+    const int64_t c_first = (int64_t)blockIdx.x * cols_per_block;
+    const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
     float *out = scores + (int64_t)r * ld;
-
-    const bool row_has_keys = cm.lo < cm.hi;
-    if (!row_has_keys) {
-        for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
+    // Columns of this chunk that can hold keys: [c_begin, c_end).  A flat column is a token position,
+    // so the chunk is cut to the row's range [lo, hi) (its start kept on a 64-column group); a paged
+    // column maps through the page list, and the whole chunk is kept.  The columns cut off are -inf.
+    int64_t c_begin = c_first, c_end = c_last;
+    if constexpr (MODE == kModeFlat) {
+        c_begin = max(c_first, cm.lo / 64 * 64);
+        c_end = min(c_last, cm.hi);
+    }
+    if (cm.lo >= cm.hi || c_begin >= c_end) {  // no keys here (the DMAs below need a row of keys)
+        for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
         return;
     }
+    for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
+        out[c] = -INFINITY;
+    for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
+        out[c] = -INFINITY;
     u32x4 qa[4][4];
     const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
 #pragma unroll

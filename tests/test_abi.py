@@ -63,6 +63,11 @@ def test_index_score_validation(L):
     assert call(1, ctypes.byref(nr), 64, 128, None, 0, 0, 100) == L.LSA_ERR_INVALID
     big = _rows(L, n_rows=70000)
     assert call(1, ctypes.byref(big), 64, 128, None, 0, 0, 100) == L.LSA_ERR_UNSUPPORTED
+    bad_min = _rows(L)
+    bad_min.min_kv_len = 101  # above max_kv_len
+    assert call(1, ctypes.byref(bad_min), 64, 128, None, 0, 0, 100) == L.LSA_ERR_INVALID
+    bad_min.min_kv_len = -1
+    assert call(1, ctypes.byref(bad_min), 64, 128, None, 0, 0, 100) == L.LSA_ERR_INVALID
     assert b"ld_scores" in lib.lsa_last_error() or lib.lsa_last_error()
 
 

@@ -459,6 +459,22 @@ def test_layer_hi_vs_oracle(B):
     log(f"HI B={B}: needles picked {hits}/{sum(len(p) for p in x['needles'])}")
 
 
+def test_layer_hi_all_rows_bound():
+    # min_kv_len >= hi_min_len lets the layer skip the flat passes and the row-role pass; the result is
+    # bit for bit that of the gated run (min_kv_len = 0)
+    lengths = [40000, 25000]
+    x, sb_off, km = _hi_setup(lengths, M=24, B=128, hi_min_len=20000)
+    c = x["cfg"]
+    r0 = rows_of(x)
+    r1 = lsa.RowsDesc(r0.kv_off, r0.row_seq, r0.row_pos, r0.max_kv_len, min(lengths))
+    a = lsa.lsa_layer_fwd(c, r0, x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"], sb_off=sb_off.to(DEV),
+                          k_mean=km)
+    b = lsa.lsa_layer_fwd(c, r1, x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"], sb_off=sb_off.to(DEV),
+                          k_mean=km)
+    assert torch.equal(a[0], b[0])
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16)) and torch.equal(a[2], b[2])
+
+
 def test_cli_reuse_layer():
     x = synth.decode_batch([7000, 3000], device=DEV, seed=9, needles=4)
     c = x["cfg"]

@@ -47,6 +47,7 @@ struct ColMap {
     int64_t last_page;  // PAGEMEAN: pages p <= last_page are causal and exist
     int G;              // PAGEMEAN: sub-blocks per page
     int P;              // PAGED: page size
+    int p_shift;        // PAGED: log2(P) when P is a power of two, else -1
     const int32_t *page_row;
     int M;
 };
@@ -63,6 +64,7 @@ __device__ inline ColMap make_colmap(const RowInfo &ri, const SiRanges &g, const
     m.last_page = -1;
     m.G = 1;
     m.P = P;
+    m.p_shift = P > 0 && (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
     m.page_row = pages ? pages + (int64_t)r * M : nullptr;
     m.M = M;
     if (MODE == kModePageMean) {
@@ -78,6 +80,13 @@ __device__ inline ColMap make_colmap(const RowInfo &ri, const SiRanges &g, const
     return m;
 }
 
+// Page slot of a page-mapped column (columns stay below M P < 2^31): a shift for the usual power-of-two
+// page size instead of a division.
+__device__ inline uint32_t page_slot(const ColMap &m, uint32_t c)
+{
+    return m.p_shift >= 0 ? c >> m.p_shift : c / (uint32_t)m.P;
+}
+
 // Key row of column c (or -1 when the column holds no score).
 template <int MODE>
 __device__ inline int64_t col_key(const ColMap &m, int64_t c)
@@ -85,13 +94,13 @@ __device__ inline int64_t col_key(const ColMap &m, int64_t c)
     if (MODE == kModeFlat) {
         return (c >= m.lo && c < m.hi) ? m.base + c : -1;
     } else if (MODE == kModePaged) {
-        int64_t slot = c / m.P;
+        const int64_t slot = page_slot(m, (uint32_t)c);
         if (slot >= m.M)
             return -1;
         int64_t pg = m.page_row[slot];
         if (pg < 0)
             return -1;
-        int64_t s = pg * m.P + c % m.P;
+        int64_t s = pg * m.P + (c - slot * m.P);
         return (s >= m.lo && s < m.hi) ? m.base + s : -1;
     } else {
         return (c < m.nsb && c / m.G <= m.last_page) ? m.base + c : -1;
@@ -412,7 +421,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             return c0;
         } else {
             // (columns and slots fit in 32 bits; readfirstlane keeps the index in scalar registers)
-            const int slot = __builtin_amdgcn_readfirstlane((int)(c0 / cm.P));
+            const int slot = __builtin_amdgcn_readfirstlane((int)page_slot(cm, (uint32_t)c0));
             if (slot >= cm.M)
                 return -1;
             const int64_t pg = pages[(int64_t)r * M + slot];

@@ -3,7 +3,8 @@
 //
 // Keys are the order-preserving 32-bit images of the scores (-0 folded onto +0); -inf and NaN are
 // not candidates and map to key 0.  The selection runs in levels.  A block holds a segment of
-// 64 * NT keys in registers (thread t holds positions 64 t .. 64 t + 63 of the segment) and picks
+// 64 * NT keys in registers (thread t holds positions 64 t .. 64 t + 63 of the segment; 16 per thread
+// when a whole row has at most 16 * NT columns) and picks
 // its best k under (key desc, position asc) by MSB-first radix select: three digits (bits 31..21,
 // 20..10, 9..0), each counted in an LDS histogram whose suffix sums locate the bin of the k-th key;
 // keys above that bin are picked and, once all 32 bits are fixed, ties take the lowest positions.
@@ -24,6 +25,7 @@ __host__ __device__ inline int digit_shift(int pass) { return pass == 0 ? 21 : (
 __host__ __device__ inline int digit_width(int pass) { return pass == 2 ? 10 : 11; }
 
 constexpr int kVpt = 64;                        // keys per thread
+constexpr int kSmallVpt = 16;                   // keys per thread when a row has at most 4096 columns
 constexpr int kSegThreads = 256;
 constexpr int kSeg = kVpt * kSegThreads;        // 16384
 constexpr int kMaxLocalK = 4096;
@@ -75,15 +77,15 @@ constexpr int kHistWords = kBins * kCopies + kWave;  // + one dummy word per lan
 constexpr int kStageWords = 2 * (kMaxLocalK + kWave);
 constexpr int kLdsWords = kHistWords > kStageWords ? kHistWords : kStageWords;
 
-template <int NT>
-__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[kVpt], uint32_t k,
+template <int NT, int VPT>
+__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[VPT], uint32_t k,
                                                                  uint32_t *hist, uint32_t *scratch, int *s_d,
                                                                  uint32_t *s_above, uint32_t *s_bin)
 {
     Selection sel{0u, 0, k, false, false};
     uint32_t cnt = 0;
 #pragma unroll
-    for (int m = 0; m < kVpt; ++m)
+    for (int m = 0; m < VPT; ++m)
         cnt += key[m] != 0 ? 1u : 0u;
     uint32_t e0, e1, total, t1;
     block_scan2<NT>(cnt, 0, e0, e1, total, t1, scratch);
@@ -104,14 +106,17 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
         // keys whose top `consumed` bits equal the prefix: (x & pmask) == pval (uniform scalars)
         const uint32_t pmask = sel.consumed == 0 ? 0u : ~0u << (32 - sel.consumed);
         const uint32_t pval = sel.consumed == 0 ? 0u : sel.prefix << (32 - sel.consumed);
-        // Key 0 (not a candidate) is not counted: it goes to the dummy word like the keys outside the
-        // prefix (segments padded with zeros would otherwise pile their atomics onto bin 0).  No
-        // candidate key falls in pass-0 bin 0 (its top 11 bits would make it -inf or a NaN).
+        // Pass-0 bin 0 holds key 0 only (a candidate's top 11 bits are never all zero: that would make
+        // it -inf or a NaN): its adds go to the dummy word like those of keys outside the prefix, so
+        // segments padded with zeros do not pile their atomics onto one bin.  (The test is on the
+        // digit, which changes with the pass, not on the key: the compiler would keep 64 loop-invariant
+        // key tests in scalar registers across the passes.)
 #pragma unroll
-        for (int m = 0; m < kVpt; ++m) {
+        for (int m = 0; m < VPT; ++m) {
             const uint32_t x = key[m];
-            const bool take = (x & pmask) == pval && x != 0u;
-            atomicAdd(&hist[take ? kCopies * ((x >> shift) & dmask) + copy : dummy], 1u);
+            const uint32_t d = (x >> shift) & dmask;
+            const bool take = (x & pmask) == pval && (d != 0u || pass != 0);
+            atomicAdd(&hist[take ? kCopies * d + copy : dummy], 1u);
         }
         __syncthreads();
         // Suffix sums (keys in bin b or above): thread t owns bins [kPer t, kPer t + kPer).
@@ -166,8 +171,8 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
 // Writes the picks of a selection, in position order, to stage_key / stage_li (key and index in
 // the segment) at slots 0 .. n - 1 and returns n; keys not picked go to per-lane dummy slots
 // stage[kMaxLocalK + lane].
-template <int NT>
-__device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&key)[kVpt], const Selection &sel,
+template <int NT, int VPT>
+__device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&key)[VPT], const Selection &sel,
                                                               uint32_t *scratch, uint32_t *stage_key,
                                                               uint32_t *stage_li, uint32_t first_li)
 {
@@ -189,12 +194,17 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
         // keys >= t_gt, numbered in position order.
         uint32_t cg = 0;
 #pragma unroll
-        for (int m = 0; m < kVpt; ++m)
-            cg += key[m] >= t_gt ? 1u : 0u;
+        for (int m = 0; m < VPT; ++m) {
+            // (an opaque copy: the compiler would otherwise keep all the compare masks of this loop
+            // in scalar registers for the loop below, and spill them)
+            uint32_t x = key[m];
+            asm volatile("" : "+v"(x));
+            cg += x >= t_gt ? 1u : 0u;
+        }
         uint32_t bg, unused, tg, unused2;
         block_scan2<NT>(cg, 0, bg, unused, tg, unused2, scratch);
 #pragma unroll
-        for (int m = 0; m < kVpt; ++m) {
+        for (int m = 0; m < VPT; ++m) {
             const bool g = key[m] >= t_gt;
             const uint32_t slot = g ? bg : dummy;
             stage_key[slot] = key[m];
@@ -206,7 +216,7 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
     // Flags of this thread's keys as bit masks (bit m: key m).
     uint64_t gbits = 0, ebits = 0;
 #pragma unroll
-    for (int m = 0; m < kVpt; ++m) {
+    for (int m = 0; m < VPT; ++m) {
         gbits |= (uint64_t)(key[m] >= t_gt ? 1u : 0u) << m;
         ebits |= (uint64_t)(key[m] == t_eq ? 1u : 0u) << m;
     }
@@ -214,7 +224,7 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
     uint32_t bg, be, tg, te;
     block_scan2<NT>(cg, ce, bg, be, tg, te, scratch);
 #pragma unroll
-    for (int m = 0; m < kVpt; ++m) {
+    for (int m = 0; m < VPT; ++m) {
         const bool g = (gbits >> m) & 1u, e = (ebits >> m) & 1u;
         const bool pick = g || (e && be < sel.k_rem);
         const uint32_t slot = pick ? bg + (be < sel.k_rem ? be : sel.k_rem) : dummy;
@@ -231,7 +241,7 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
 // otherwise candidates [seg * 64 NT, ...) of row r's list of n_in.  FINAL: the picks (positions)
 // go to idx[r][0 .. k), padded with -1; otherwise to the next list at [seg * k, seg * k + k),
 // padded with key 0.
-template <int NT, bool SRC_SCORES, bool FINAL>
+template <int NT, int VPT, bool SRC_SCORES, bool FINAL>
 __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict__ scores, int64_t ld, int64_t n_in,
                                                          const int32_t *__restrict__ pages, int M, int P,
                                                          const uint32_t *__restrict__ in_key,
@@ -248,16 +258,19 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
     __shared__ uint32_t scratch[2 * NT / kWave];
     __shared__ int s_d;
     __shared__ uint32_t s_above, s_bin;
-    const int64_t seg_base = (int64_t)seg * (kVpt * NT);
-    const int64_t base = seg_base + (int64_t)kVpt * threadIdx.x;  // this thread's first element
+    const int64_t seg_base = (int64_t)seg * (VPT * NT);
+    const int64_t base = seg_base + (int64_t)VPT * threadIdx.x;  // this thread's first element
     const int32_t *page_row = pages ? pages + (int64_t)r * M : nullptr;
-    uint32_t key[kVpt];
+    // page slot of column c (c < M P < 2^31): a shift for a power-of-two page size
+    const int p_shift = (P & (P - 1)) == 0 ? __builtin_ctz((unsigned)P) : -1;
+    auto slot_of = [&](uint32_t c) { return p_shift >= 0 ? c >> p_shift : c / (uint32_t)P; };
+    uint32_t key[VPT];
     if constexpr (SRC_SCORES) {
         const float *row = scores + (int64_t)r * ld;
-        if (base + kVpt <= n_in && (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
+        if (base + VPT <= n_in && (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
             const float4 *src = reinterpret_cast<const float4 *>(row + base);
 #pragma unroll
-            for (int q = 0; q < kVpt / 4; ++q) {
+            for (int q = 0; q < VPT / 4; ++q) {
                 const float4 v = src[q];
                 key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
                 key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
@@ -269,7 +282,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
             // float4 that straddles it.
             const float4 *src = reinterpret_cast<const float4 *>(row + base);
 #pragma unroll
-            for (int q = 0; q < kVpt / 4; ++q) {
+            for (int q = 0; q < VPT / 4; ++q) {
                 const int64_t c = base + 4 * q;
                 float4 v = float4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
                 if (c + 4 <= n_in) {
@@ -286,7 +299,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < kVpt; ++m) {
+            for (int m = 0; m < VPT; ++m) {
                 const int64_t c = base + m;
                 const float v = c < n_in ? row[c] : -INFINITY;
                 key[m] = is_candidate(v) ? float_order_key(v) : 0u;
@@ -294,9 +307,9 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
         }
         if (page_row) {
 #pragma unroll
-            for (int q = 0; q < kVpt / 16; ++q) {
+            for (int q = 0; q < VPT / 16; ++q) {
                 const int64_t c = base + 16 * q;
-                const bool ok = c < n_in && page_row[(uint32_t)c / (uint32_t)P] >= 0;
+                const bool ok = c < n_in && page_row[slot_of((uint32_t)c)] >= 0;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     key[16 * q + i] = ok ? key[16 * q + i] : 0u;
@@ -304,23 +317,23 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
         }
     } else {
         const uint32_t *src = in_key + (int64_t)r * in_ld;
-        if (base + kVpt <= n_in) {
+        if (base + VPT <= n_in) {
             const uint4 *s4 = reinterpret_cast<const uint4 *>(src + base);
 #pragma unroll
-            for (int q = 0; q < kVpt / 4; ++q) {
+            for (int q = 0; q < VPT / 4; ++q) {
                 const uint4 v = s4[q];
                 key[4 * q] = v.x, key[4 * q + 1] = v.y, key[4 * q + 2] = v.z, key[4 * q + 3] = v.w;
             }
         } else {
 #pragma unroll
-            for (int m = 0; m < kVpt; ++m)
+            for (int m = 0; m < VPT; ++m)
                 key[m] = base + m < n_in ? src[base + m] : 0u;
         }
     }
-    const Selection sel = block_select<NT>(key, (uint32_t)k, lds, scratch, &s_d, &s_above, &s_bin);
+    const Selection sel = block_select<NT, VPT>(key, (uint32_t)k, lds, scratch, &s_d, &s_above, &s_bin);
     uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
     __syncthreads();  // the histograms are no longer read
-    const uint32_t n_sel = block_emit<NT>(key, sel, scratch, stage_key, stage_li, (uint32_t)(kVpt * threadIdx.x));
+    const uint32_t n_sel = block_emit<NT, VPT>(key, sel, scratch, stage_key, stage_li, (uint32_t)(VPT * threadIdx.x));
     __syncthreads();
     // Copy-out in slot order (coalesced), with positions computed for the picks only.
     for (int i = threadIdx.x; i < k; i += NT) {
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
         if ((uint32_t)i < n_sel && c < n_in) {  // (a pick is always below n_in: keys past it are 0)
             kv = stage_key[i];
             if constexpr (SRC_SCORES)
-                pos = page_row ? page_row[(uint32_t)c / (uint32_t)P] * P + (int32_t)((uint32_t)c % (uint32_t)P)
+                pos = page_row ? page_row[slot_of((uint32_t)c)] * P + (int32_t)((uint32_t)c - slot_of((uint32_t)c) * (uint32_t)P)
                                : (int32_t)c;
             else
                 pos = in_pos[(int64_t)r * in_ld + c];
@@ -374,9 +387,16 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     int64_t n_seg, l0, l1;
     topk2_sizes(n_cols, k, n_seg, l0, l1);
     if (n_seg <= 1) {
-        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, true, true>), dim3(1, n_rows), dim3(kSegThreads), 0,
-                           stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, nullptr, nullptr, 0, idx,
-                           gate.row_mode, gate.want);
+        // One segment per row: with at most 4096 columns, 16 keys per thread (a quarter of the per-key
+        // work of the 16384-column segment).
+        if (n_cols <= kSmallVpt * kSegThreads)
+            hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kSmallVpt, true, true>), dim3(1, n_rows),
+                               dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
+                               nullptr, nullptr, 0, idx, gate.row_mode, gate.want);
+        else
+            hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, true>), dim3(1, n_rows), dim3(kSegThreads),
+                               0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, nullptr, nullptr, 0,
+                               idx, gate.row_mode, gate.want);
         return hipGetLastError();
     }
     // Two candidate buffers (key, position) with row strides lda >= l0 and ldb >= l1, used in turn.
@@ -389,7 +409,7 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     uint32_t *key_b = (uint32_t *)p;
     p += align_up((size_t)n_rows * ldb * 4);
     int32_t *pos_b = (int32_t *)p;
-    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, true, false>), dim3((unsigned)n_seg, n_rows),
+    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, false>), dim3((unsigned)n_seg, n_rows),
                        dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, key_a,
                        pos_a, lda, nullptr, gate.row_mode, gate.want);
     int64_t n_in = l0;
@@ -397,7 +417,7 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     while (n_in > kSeg) {  // reduce the candidate lists further
         const int64_t segs = (n_in + kSeg - 1) / kSeg;
         const int64_t n_out = segs * k;
-        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, false, false>), dim3((unsigned)segs, n_rows),
+        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, false>), dim3((unsigned)segs, n_rows),
                            dim3(kSegThreads), 0, stream, nullptr, 0, n_in, nullptr, 0, 1, in_a ? key_a : key_b,
                            in_a ? pos_a : pos_b, in_a ? lda : ldb, k, in_a ? key_b : key_a, in_a ? pos_b : pos_a,
                            in_a ? ldb : lda, nullptr, gate.row_mode, gate.want);
@@ -407,7 +427,7 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     const uint32_t *fk = in_a ? key_a : key_b;
     const int32_t *fp = in_a ? pos_a : pos_b;
     const int64_t fld = in_a ? lda : ldb;
-    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0, stream,
+    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0, stream,
                        nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx, gate.row_mode,
                        gate.want);
     return hipGetLastError();

@@ -527,20 +527,21 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 // Multi-row bf16 kernel (prefill): the 16 rows of a group share every key tile, so the keys are read
 // from HBM once per group instead of once per row and the work becomes matrix-core bound.
 //
-// Block = 8 waves; wave w owns rows 16 G + 2w and 16 G + 2w + 1 (both 64x128 query blocks stay in
-// VGPRs).  Keys arrive in stages of 128 (32 KB) by LDS DMA, double-buffered, one barrier per
-// stage.  Inside a stage the 16-byte chunk c of key k is stored at slot 16 k + (c ^ (k % 16)), so
-// the 16 lanes that read one MFMA operand hit 16 different bank groups.  The epilogue reduces the
-// two rows over the 4 lane groups with two lane swaps (each row keeps half of the groups after the
-// first).
+// Block = 16 waves, one row each (its 64x128 query block in VGPRs): four waves per SIMD at 128
+// registers, so one wave's ReLU / weight epilogue runs beside another's matrix products.  Keys arrive
+// in stages of 128 (32 KB) by LDS DMA, double-buffered, one barrier per stage.  Inside a stage the
+// 16-byte chunk c of key k is stored at slot 16 k + (c ^ (k % 16)), so the 16 lanes that read one
+// MFMA operand hit 16 different bank groups.  Four tiles are scored before their results are stored:
+// lane group g stores tile g, so one store instruction writes 256 contiguous bytes.
 
-constexpr int kGroupWaves = 8;
+constexpr int kGroupWaves = 16;
 constexpr int kGroupThreads = kGroupWaves * kWave;
 constexpr int kStageKeys = 128;
 constexpr int kStageTiles = kStageKeys / kTile;              // 8
 constexpr int kStageElems = kStageKeys * kDim;               // bf16 elements per stage (32 KB)
 constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 32 wave-wide 1 KB DMA writes
 constexpr int kMinGroupedRows = 64;                          // fewer rows: the per-row kernel only
+static_assert(kGroupWaves == kGroupRows, "one row per wave");
 
 __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     RowsDev rows, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ keys,
@@ -556,25 +557,24 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageElems];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = lane_id();
     const int n = lane & 15;
     const int g = lane >> 4;
-    const int rl0 = 2 * wave;  // local row index of this wave's first row
-    const int r0 = grp * kGroupRows + rl0;
+    const int r = grp * kGroupRows + wave;
 
     // Column ranges (columns are below 2^31): every valid row scores [k_sink, hi_r) with hi_r the
     // end of its mid region cut at L; lanes 0..15 of every wave take one row each and reduce.
-    const RowInfo ri0 = row_info(rows, r0);
+    const RowInfo ri0 = row_info(rows, grp * kGroupRows);
     const int L = (int)ri0.L;
     const int64_t base = ri0.base;
-    auto row_hi = [&](int r) {
-        const RowInfo ri = row_info(rows, r);
+    auto row_hi = [&](int rr) {
+        const RowInfo ri = row_info(rows, rr);
         const SiRanges gi = si_ranges(ri, k_sink, k_swa);
         return (int)(gi.mid_hi < ri.L ? gi.mid_hi : ri.L);
     };
     const int lo = k_sink;
-    const int hiA = row_hi(r0), hiB = row_hi(r0 + 1);
+    const int my_hi = row_hi(r);
     int u_hi = row_hi(grp * kGroupRows + n);
     for (int o = 1; o < 16; o <<= 1)
         u_hi = max(u_hi, __shfl_xor(u_hi, o, kWave));
@@ -592,35 +592,34 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     const int cmp_hi = min(c_begin + st_end * kStageKeys, c_end);
 
     // Columns outside the computed stages hold no score for any row of the group.
-    for (int rl = 0; rl < kGroupRows; ++rl) {
-        float *o = scores + (int64_t)(grp * kGroupRows + rl) * ld;
-        for (int64_t c = c_begin + tid; c < cmp_lo; c += kGroupThreads)
+    {
+        float *o = scores + (int64_t)r * ld;
+        for (int64_t c = c_begin + lane; c < cmp_lo; c += kWave)
             o[c] = -INFINITY;
-        for (int64_t c = cmp_hi + tid; c < c_end; c += kGroupThreads)
+        for (int64_t c = cmp_hi + lane; c < c_end; c += kWave)
             o[c] = -INFINITY;
     }
 
     if (st_first < st_end) {
-        // A operands of both rows, and the head weights of the 16 heads each lane ends up holding.
-        u32x4 qa[2][4][4];
-        float wv[2][4][4];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint16_t *qrow = q_idx + (int64_t)(r0 + j) * kHeads * kDim;
+        // A operands of the row, and the head weights of the 16 heads each lane ends up holding.
+        u32x4 qa[4][4];
+        float wv[4][4];
+        {
+            const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    qa[j][mt][ks] = src[4 * ks];
-                f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)(r0 + j) * kHeads + mt * 16 + 4 * g);
+                    qa[mt][ks] = src[4 * ks];
+                f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    wv[j][mt][i] = v[i];
+                    wv[mt][i] = v[i];
             }
         }
-        // DMA j = wave + 8 jj of a stage fills slots 64 j .. 64 j + 63, i.e. keys 4 j .. 4 j + 3: this
-        // lane moves chunk c16 of key 4 wave + 32 jj + g (the same chunk for every jj).
+        // DMA j = wave + 16 jj of a stage fills slots 64 j .. 64 j + 63, i.e. keys 4 j .. 4 j + 3: this
+        // lane moves chunk c16 of key 4 wave + 64 jj + g (the same chunk for both jj).
         const int kk0 = 4 * wave + g;
         const int c16 = n ^ (kk0 & 15);
         const uint16_t *kseq = keys + base * kDim;
@@ -630,14 +629,40 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
             const int lim = L - 1 - col0;  // keys past the sequence re-read its last key
 #pragma unroll
             for (int jj = 0; jj < kStageDma / kGroupWaves; ++jj) {
-                const int kk = min(kk0 + 32 * jj, lim);
+                const int kk = min(kk0 + 64 * jj, lim);
                 __builtin_amdgcn_global_load_lds((glb_void *)(ks0 + kk * kDim + c16 * 8),
                                                  (lds_void *)(buf + (wave + kGroupWaves * jj) * kWave * 8), 16, 0, 0);
             }
         };
-        float *outA = scores + (int64_t)r0 * ld;
-        float *outB = outA + ld;
-        const int my_hi = g < 2 ? hiA : hiB;
+        float *out = scores + (int64_t)r * ld;
+
+        // Score of tile tt of a stage for key n (every lane group ends with the same value).
+        auto score_tile = [&](const uint16_t *buf, int tt) __attribute__((always_inline)) -> float {
+            u32x4 b[4];
+            const uint16_t *krow = buf + (tt * kTile + n) * kDim;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+            f32x4 acc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
+                                                                      acc[mt], 0, 0, 0);
+            }
+            float v = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v += wv[mt][i] * relu(acc[mt][i]);
+            return sum_xor32(sum_xor16(v));
+        };
 
         // One stage: wait for its DMA, start the next stage's into the other buffer, score 8 tiles.
         auto run_stage = [&](int st, const uint16_t *buf, uint16_t *next) __attribute__((always_inline)) {
@@ -646,52 +671,19 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
             if (st + 1 < st_end)
                 issue_stage(st + 1, next);
             const int col0 = c_begin + st * kStageKeys;
-            float *sA = outA + col0;
-            float *sB = outB + col0;
             const int rel_lo = lo - col0, rel_hi = min(my_hi, c_end) - col0, rel_end = c_end - col0;
-#pragma unroll 2  // (a full unroll spills)
-            for (int tt = 0; tt < kStageTiles; ++tt) {
-                u32x4 b[4];
-                const uint16_t *krow = buf + (tt * kTile + n) * kDim;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
-                f32x4 acc[2][4];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int mt = 0; mt < 4; ++mt)
-                            acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, qa[j][mt][ks]), bb, acc[j][mt], 0, 0, 0);
+#pragma unroll 1
+            for (int t4 = 0; t4 < kStageTiles; t4 += 4) {
+                // one tile at a time (four in flight would not fit in 128 registers)
+                float v = 0.0f;
+#pragma unroll 1
+                for (int q = 0; q < 4; ++q) {
+                    const float vq = score_tile(buf, t4 + q);
+                    v = g == q ? vq : v;
                 }
-                float vA = 0.0f, vB = 0.0f;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        vA += wv[0][mt][i] * relu(acc[0][mt][i]);
-                        vB += wv[1][mt][i] * relu(acc[1][mt][i]);
-                    }
-                // Groups 0, 1 keep row A and take the other half of its partials from groups 2, 3;
-                // groups 2, 3 do the same for row B; then the pairs (0,1) and (2,3) combine.
-                const float keep = sum_xor16(sum_halves32(vA, vB));
-                const int rel = tt * kTile + n;
-                const bool valid = rel >= rel_lo && rel < rel_hi;
-                const float val = valid ? keep : -INFINITY;
-                if (rel < rel_end) {
-                    if (g == 0)
-                        sA[rel] = val;
-                    else if (g == 2)
-                        sB[rel] = val;
-                }
+                const int rel = (t4 + g) * kTile + n;
+                if (rel < rel_end)
+                    out[col0 + rel] = rel >= rel_lo && rel < rel_hi ? v : -INFINITY;
             }
         };
         if (st_first & 1)

@@ -2,9 +2,9 @@
 // [paper] §3.3, which selects Ksparse tokens among recalled pages).
 //
 // Keys are the order-preserving 32-bit images of the scores (-0 folded onto +0); -inf and NaN are
-// not candidates and map to key 0.  The selection runs in levels.  A block holds a segment of
-// 64 * NT keys in registers (thread t holds positions 64 t .. 64 t + 63 of the segment; 16 per thread
-// when a whole row has at most 16 * NT columns) and picks
+// not candidates and map to key 0.  The selection runs in levels.  A block of 512 threads holds a
+// segment of 16384 keys in registers (thread t holds positions 32 t .. 32 t + 31 of the segment; a
+// whole row of at most 4096 columns goes to one block of 256 threads x 16 keys) and picks
 // its best k under (key desc, position asc) by MSB-first radix select: three digits (bits 31..21,
 // 20..10, 9..0), each counted in an LDS histogram whose suffix sums locate the bin of the k-th key;
 // keys above that bin are picked and, once all 32 bits are fixed, ties take the lowest positions.
@@ -24,26 +24,38 @@ constexpr int kBins = 2048;
 __host__ __device__ inline int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __host__ __device__ inline int digit_width(int pass) { return pass == 2 ? 10 : 11; }
 
-constexpr int kVpt = 64;                        // keys per thread
-constexpr int kSmallVpt = 16;                   // keys per thread when a row has at most 4096 columns
-constexpr int kSegThreads = 256;
-constexpr int kSeg = kVpt * kSegThreads;        // 16384
+#ifndef LSA_TOPK_THREADS
+#define LSA_TOPK_THREADS 512
+#endif
+constexpr int kSeg = 16384;                     // keys per segment (one block)
+constexpr int kSegThreads = LSA_TOPK_THREADS;
+constexpr int kVpt = kSeg / kSegThreads;        // keys per thread
+constexpr int kSmallThreads = 256;
+constexpr int kSmallVpt = 16;                   // a row of at most 4096 columns: one block of 256 x 16
 constexpr int kMaxLocalK = 4096;
 
 // Exclusive prefix sums over threads (in thread order) of two counters, and their totals.
 // scratch: 2 * NT / 64 words of LDS.
+// Inclusive prefix sum over the 64 lanes of a wave in registers (DPP): row shifts 1, 2, 4, 8 scan
+// each row of 16 lanes, then row broadcasts add lane 15 to rows 1 and 3 and lane 31 to rows 2 and 3.
+__device__ __attribute__((always_inline)) inline uint32_t wave_incl_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 template <int NT>
 __device__ __attribute__((always_inline)) inline void block_scan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb, uint32_t &ta, uint32_t &tb,
                                    uint32_t *scratch)
 {
     constexpr int NW = NT / kWave;
     const int lane = lane_id(), w = threadIdx.x >> 6;
-    uint32_t ia = a, ib = b;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t ya = (uint32_t)__shfl_up((int)ia, o, kWave), yb = (uint32_t)__shfl_up((int)ib, o, kWave);
-        if (lane >= o)
-            ia += ya, ib += yb;
-    }
+    const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
     if (lane == kWave - 1)
         scratch[w] = ia, scratch[NW + w] = ib;
     __syncthreads();
@@ -389,9 +401,9 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     if (n_seg <= 1) {
         // One segment per row: with at most 4096 columns, 16 keys per thread (a quarter of the per-key
         // work of the 16384-column segment).
-        if (n_cols <= kSmallVpt * kSegThreads)
-            hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kSmallVpt, true, true>), dim3(1, n_rows),
-                               dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
+        if (n_cols <= kSmallVpt * kSmallThreads)
+            hipLaunchKernelGGL((topk_level_kernel<kSmallThreads, kSmallVpt, true, true>), dim3(1, n_rows),
+                               dim3(kSmallThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
                                nullptr, nullptr, 0, idx, gate.row_mode, gate.want);
         else
             hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, true>), dim3(1, n_rows), dim3(kSegThreads),

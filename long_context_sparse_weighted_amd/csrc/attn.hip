@@ -62,47 +62,44 @@ struct SelList {
 __device__ inline int compact_picks(const int32_t *pick_row, int k_sparse, const SiRanges &g, int32_t *sparse,
                                     int32_t *scan_tmp)
 {
+    // Thread t takes entries [t per, t per + per) (per <= kMaxSparse / 256 = 16 for the block sizes
+    // used here), read once into registers with the entry before them (for the repeat test).
+    constexpr int kMaxPer = kMaxSparse / 256;
     const int nt = blockDim.x;
     const int tid = threadIdx.x;
     const int per = (k_sparse + nt - 1) / nt;
     const int i0 = tid * per;
+    int32_t v[kMaxPer];
+    bool ok[kMaxPer];
+    int32_t prev = (i0 > 0 && i0 <= k_sparse) ? pick_row[i0 - 1] : INT32_MIN;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+        v[j] = (j < per && i0 + j < k_sparse) ? pick_row[i0 + j] : INT32_MIN;
     int cnt = 0;
-    for (int i = i0; i < i0 + per && i < k_sparse; ++i) {
-        int32_t s = pick_row[i];
-        bool ok = s >= g.mid_lo && s < g.mid_hi && (i == 0 || pick_row[i - 1] != s);
-        cnt += ok ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+        const int32_t s = v[j];
+        ok[j] = j < per && i0 + j < k_sparse && s >= g.mid_lo && s < g.mid_hi && (i0 + j == 0 || s != prev);
+        prev = s;
+        cnt += ok[j] ? 1 : 0;
     }
-    // Exclusive scan of the per-thread counts: wave-level shuffles, then the wave totals.
+    // Exclusive scan of the per-thread counts: the wave's in registers, then the wave totals.
     const int lane = lane_id(), wave = tid >> 6, n_waves = nt >> 6;
-    int incl = cnt;
-    for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(incl, o, kWave);
-        if (lane >= o)
-            incl += y;
-    }
+    const int incl = (int)wave_incl_scan((uint32_t)cnt);
     if (lane == kWave - 1)
-        scan_tmp[nt + 1 + wave] = incl;
+        scan_tmp[wave] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int acc = 0;
-        for (int i = 0; i < n_waves; ++i) {
-            int v = scan_tmp[nt + 1 + i];
-            scan_tmp[nt + 1 + i] = acc;
-            acc += v;
-        }
-        scan_tmp[nt] = acc;
+    int before = 0, total = 0;
+    for (int i = 0; i < n_waves; ++i) {
+        const int x = scan_tmp[i];
+        before += i < wave ? x : 0;
+        total += x;
     }
-    __syncthreads();
-    scan_tmp[tid] = scan_tmp[nt + 1 + wave] + incl - cnt;
-    __syncthreads();
-    int o = scan_tmp[tid];
-    for (int i = i0; i < i0 + per && i < k_sparse; ++i) {
-        int32_t s = pick_row[i];
-        bool ok = s >= g.mid_lo && s < g.mid_hi && (i == 0 || pick_row[i - 1] != s);
-        if (ok)
-            sparse[o++] = s;
-    }
-    int total = scan_tmp[nt];
+    int o = before + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+        if (ok[j])
+            sparse[o++] = v[j];
     __syncthreads();
     return total;
 }

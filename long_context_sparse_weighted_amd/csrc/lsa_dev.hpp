@@ -153,6 +153,19 @@ __device__ inline int lane_id() { return __lane_id(); }
 // Cross-lane pair sums on the VALU with the CDNA4 lane swaps (no LDS round trip).
 // permlane32_swap(a, b) exchanges the upper 32 lanes of a with the lower 32 lanes of b, so the two
 // results add up to a[l] + a[l + 32] in lanes l < 32 and b[l - 32] + b[l] in lanes l >= 32.
+// Inclusive prefix sum over the 64 lanes of a wave in registers (DPP): row shifts 1, 2, 4, 8 scan
+// each row of 16 lanes, then row broadcasts add lane 15 to rows 1 and 3 and lane 31 to rows 2 and 3.
+__device__ inline uint32_t wave_incl_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
 __device__ inline float sum_halves32(float a, float b)
 {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);

@@ -36,19 +36,6 @@ constexpr int kMaxLocalK = 4096;
 
 // Exclusive prefix sums over threads (in thread order) of two counters, and their totals.
 // scratch: 2 * NT / 64 words of LDS.
-// Inclusive prefix sum over the 64 lanes of a wave in registers (DPP): row shifts 1, 2, 4, 8 scan
-// each row of 16 lanes, then row broadcasts add lane 15 to rows 1 and 3 and lane 31 to rows 2 and 3.
-__device__ __attribute__((always_inline)) inline uint32_t wave_incl_scan(uint32_t v)
-{
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return v;
-}
-
 template <int NT>
 __device__ __attribute__((always_inline)) inline void block_scan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb, uint32_t &ta, uint32_t &tb,
                                    uint32_t *scratch)

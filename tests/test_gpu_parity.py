@@ -105,16 +105,19 @@ def test_layer_bf16_grouped_rows():
     _compare_layer(x, host(idx), host(out), host(lse), w_idx, w_out, w_lse, 2e-2, OracleRanking(o, c))
 
 
-def test_index_score_bf16_page_mapped():
+@pytest.mark.parametrize("P", [128, 48])  # 48: a page size that is not a power of two (division path)
+def test_index_score_bf16_page_mapped(P):
     L = 9000
     x = custom_rows([L, 4000], [(0, L - 1), (0, 5000), (1, 3999)], attn=False)
     o = oracle_inputs(x)
     c = x["cfg"]
-    P, M = 128, 12
+    M = 12
     pages = np.full((3, M), -1, np.int32)
-    pages[0, :10] = [0, 1, 7, 8, 30, 31, 55, 60, 69, 70]        # 70 is the partial last page of L = 9000
-    pages[1, :6] = [3, 9, 20, 30, 31, 39]                       # 31 straddles mid(5000) end; 39 beyond t
-    pages[2, :5] = [0, 5, 10, 23, 31]                            # 31 is beyond L = 4000
+    # (for P = 128: 70 is the partial last page of L = 9000, 31 straddles the end of mid(5000), 39 lies
+    # beyond t = 5000 and 31 beyond L = 4000; for P = 48 the same page numbers cover other tokens)
+    pages[0, :10] = [0, 1, 7, 8, 30, 31, 55, 60, 69, 70]
+    pages[1, :6] = [3, 9, 20, 30, 31, 39]
+    pages[2, :5] = [0, 5, 10, 23, 31]
     pg = torch.from_numpy(pages).to(DEV)
     g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), pages=pg, P=P, ld=M * P + 5)
     want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
@@ -158,9 +161,10 @@ def test_topk_negative_zero_and_all_neg_inf_rows():
     assert list(got[1]) == [-1, -1, -1]
 
 
-def test_topk_page_mapped_bit_exact():
+@pytest.mark.parametrize("P", [128, 48])
+def test_topk_page_mapped_bit_exact(P):
     rng = np.random.default_rng(5)
-    P, M = 128, 40
+    M = 40
     s = _score_rows(rng, 6, M * P, "quant")
     pages = np.sort(rng.choice(5000, (6, M), replace=False), axis=1).astype(np.int32)
     pages[:, -3:] = -1

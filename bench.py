@@ -21,6 +21,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12        # B/s, MI355X HBM3E
 BF16_PEAK = 2.5e15       # FLOP/s dense MFMA
+MALL_FLUSH_BYTES = 512 << 20  # more than the 256 MB last-level (Infinity) cache: a "cold" call reads HBM
 
 
 def log(*a):
@@ -40,6 +41,29 @@ def time_on_stream(fn, steps, warmup):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps * 1e-3  # seconds per call
+
+
+def step_distribution(fn, reps, flush_bytes=0):
+    """Per-call times (us) with one event pair around each call: p10 / median / p90. With flush_bytes > 0
+    a scratch buffer of that size is written before every call (outside its events), so that the call starts
+    with the last-level cache holding none of its inputs ("cold")."""
+    import torch
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for i in range(reps):
+        if scratch is not None:
+            scratch.fill_(i & 0xff)
+        ev[i][0].record(s)
+        fn()
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    q = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    del scratch
+    return dict(p10=q(0.1), p50=q(0.5), p90=q(0.9))
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
@@ -99,6 +123,8 @@ def run_length(L, batch, steps, warmup, seed=0):
     torch.cuda.synchronize()
     t_step = (time.perf_counter() - t_start) / steps
     t_step_ev = time_on_stream(step, steps, 0)
+    warm = step_distribution(step, steps)
+    cold = step_distribution(step, steps, flush_bytes=MALL_FLUSH_BYTES)
     # The dominant kernel alone: the indexer scoring launch of the layer (same grid, same stream).
     scores = torch.empty((n, L), dtype=torch.float32, device="cuda")
     bud = (c["k_sink"], c["k_swa"], c["k_sparse"])
@@ -116,11 +142,15 @@ def run_length(L, batch, steps, warmup, seed=0):
     flops = n * (mid * 64 * 128 * 2 + (c["k_sink"] + c["k_swa"] + c["k_sparse"]) * 128 * (576 + 512) * 2)
     del scores
     res = dict(L=L, batch=n, latency_us=t_step * 1e6, latency_us_events=t_step_ev * 1e6,
+               warm_us_p10=warm["p10"], warm_us_p50=warm["p50"], warm_us_p90=warm["p90"],
+               cold_us_p10=cold["p10"], cold_us_p50=cold["p50"], cold_us_p90=cold["p90"],
                score_kernel_us=t_score * 1e6, score_kernel_bytes=k_bytes, alg_bytes=alg_bytes, flops=flops,
                hbm_frac_layer=alg_bytes / t_step / HBM_PEAK, score_kernel_gbs=k_bytes / t_score / 1e9,
                needle_recall=recall)
     log(f"[bench] L={L}: layer {t_step * 1e6:.1f} us ({res['hbm_frac_layer'] * 100:.1f}% HBM), score kernel "
-        f"{t_score * 1e6:.1f} us = {res['score_kernel_gbs']:.0f} GB/s, needle recall {recall:.3f}")
+        f"{t_score * 1e6:.1f} us = {res['score_kernel_gbs']:.0f} GB/s, needle recall {recall:.3f}; per call "
+        f"warm p10/p50/p90 {warm['p10']:.1f}/{warm['p50']:.1f}/{warm['p90']:.1f} us, cold (cache flushed) "
+        f"{cold['p10']:.1f}/{cold['p50']:.1f}/{cold['p90']:.1f} us")
     del x, layer, idx, out, lse
     torch.cuda.empty_cache()
     return res

@@ -200,29 +200,84 @@ def time_layer(x, cfg, steps, warmup, idx_row=None, sb_off=None, k_mean=None, q=
     return t, idx
 
 
-def bench_hi(steps, warmup, lengths=(262144, 524288, 1048576), batch=8):
-    """1M-context decode with HI (batch 8, P = B = 128, M = 1024) against the flat indexer on the same inputs."""
+def bench_hi(steps, warmup, lengths=(262144, 524288, 1048576), batch=8, B=128):
+    """Long-context decode with HI (batch 8, P = 128, sub-blocks of B, M = 1024) against the flat indexer
+    on the same inputs; also the one-off mean build and the per-step mean upkeep (one appended token
+    per sequence)."""
     import torch
 
     import long_context_sparse_weighted_amd as lsa
     import synth
     res = {}
     for L in lengths:
-        x = synth.hi_decode(device="cuda", L=L, batch=batch)
+        x = synth.hi_decode(device="cuda", L=L, batch=batch, B=B)
         c = x["cfg"]
-        sb_off = lsa.sb_offsets(x["lengths"], 128).to("cuda")
-        t_means = time_on_stream(lambda: lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, L), 3, 1)
-        km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, L)
+        sb_off = lsa.sb_offsets(x["lengths"], B).to("cuda")
+        t_means = time_on_stream(lambda: lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], B, L), 3, 1)
+        km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], B, L)
+        t_upkeep = time_on_stream(lambda: lsa.lsa_page_means_append(x["kv_off"], sb_off, x["k_idx"], B, km, 1),
+                                  steps, warmup)
         t_hi, idx_hi = time_layer(x, c, steps, warmup, sb_off=sb_off, k_mean=km)
         t_flat, idx_flat = time_layer(x, dict(c, hi_min_len=1 << 62), steps, warmup)
-        hi_bytes = batch * (L // 128 * 256 + 1024 * 128 * 256 + 2064 * 1152)
-        res[str(L)] = dict(hi_us=t_hi * 1e6, flat_us=t_flat * 1e6, speedup=t_flat / t_hi,
-                           page_means_build_us=t_means * 1e6, hi_alg_bytes=hi_bytes,
-                           hi_hbm_frac=hi_bytes / t_hi / HBM_PEAK,
+        # k_mean of the causal pages (stage 1), the recalled pages' keys (stage 2), the selected KV rows
+        hi_bytes = batch * (L // B * 256 + 1024 * 128 * 256 + 2064 * 1152)
+        res[str(L)] = dict(B=B, hi_us=t_hi * 1e6, flat_us=t_flat * 1e6, speedup=t_flat / t_hi,
+                           page_means_build_us=t_means * 1e6, page_means_upkeep_us=t_upkeep * 1e6,
+                           hi_alg_bytes=hi_bytes, hi_hbm_frac=hi_bytes / t_hi / HBM_PEAK,
                            same_sets_rows=int((idx_hi == idx_flat).all(1).sum().item()))
-        log(f"[bench] HI L={L}: HI {t_hi * 1e6:.1f} us, flat {t_flat * 1e6:.1f} us ({t_flat / t_hi:.2f}x), "
-            f"mean build {t_means * 1e6:.0f} us")
+        log(f"[bench] HI B={B} L={L}: HI {t_hi * 1e6:.1f} us, flat {t_flat * 1e6:.1f} us ({t_flat / t_hi:.2f}x), "
+            f"mean build {t_means * 1e6:.0f} us, per-step upkeep {t_upkeep * 1e6:.1f} us")
         del x, km
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_hi_prefill(steps, warmup, lengths=(32768, 65536, 131072, 262144, 524288, 1048576), q_len=2048):
+    """HI against the flat indexer in chunked prefill (q_len rows at the end of an L-token sequence;
+    P = 128, B = 8, M = 1024; K = 1024 picks): stage 1 = page recall (sub-block scoring, page sums,
+    page top-M), stage 2 = token scoring over the recalled pages + top-K; flat = scoring + top-K."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    res = {}
+    for L in lengths:
+        x = synth.hi_prefill(L, device="cuda", q_len=q_len)
+        c = x["cfg"]
+        P, B, M, K = c["P"], c["B"], c["M"], c["k_sparse"]
+        bud = (c["k_sink"], c["k_swa"], K)
+        rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"], L)
+        sb_off = lsa.sb_offsets(x["lengths"], B).to("cuda")
+        t_means = time_on_stream(lambda: lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], B, L), 3, 1)
+        km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], B, L)
+        ps = torch.empty((q_len, (L + P - 1) // P), dtype=torch.float32, device="cuda")
+        st = {}
+
+        def stage1():
+            st["pages"], _ = lsa.lsa_page_recall(rows, sb_off, x["q_idx"], x["w"], km, P, B, M, page_scores=ps)
+        t1 = time_on_stream(stage1, steps, warmup)
+        comp = torch.empty((q_len, M * P), dtype=torch.float32, device="cuda")
+        idx_hi = torch.empty((q_len, K), dtype=torch.int32, device="cuda")
+
+        def stage2():
+            lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], bud, scores=comp, pages=st["pages"], M=M, P=P)
+            lsa.lsa_topk(comp, K, pages=st["pages"], P=P, idx=idx_hi)
+        t2 = time_on_stream(stage2, steps, warmup)
+        del comp
+        scores = torch.empty((q_len, L), dtype=torch.float32, device="cuda")
+        idx_flat = torch.empty((q_len, K), dtype=torch.int32, device="cuda")
+
+        def flat():
+            lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], bud, scores=scores)
+            lsa.lsa_topk(scores, K, idx=idx_flat)
+        tf = time_on_stream(flat, steps, warmup)
+        res[str(L)] = dict(stage1_ms=t1 * 1e3, stage2_ms=t2 * 1e3, hi_total_ms=(t1 + t2) * 1e3, flat_ms=tf * 1e3,
+                           speedup=tf / (t1 + t2), page_means_build_ms=t_means * 1e3,
+                           same_sets_rows=int((idx_hi == idx_flat).all(1).sum().item()))
+        log(f"[bench] HI prefill L={L}: stage 1 {t1 * 1e3:.3f} ms, stage 2 {t2 * 1e3:.3f} ms, HI "
+            f"{(t1 + t2) * 1e3:.3f} ms, flat {tf * 1e3:.3f} ms ({tf / (t1 + t2):.2f}x), mean build "
+            f"{t_means * 1e3:.2f} ms")
+        del x, km, ps, scores, st
         torch.cuda.empty_cache()
     return res
 
@@ -320,7 +375,7 @@ def main():
     ap.add_argument("--lengths", default="131072,1048576")
     ap.add_argument("--hi-lengths", default="262144,524288,1048576", help="KV lengths of the HI workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="decode", choices=["decode", "hi", "prefill", "ragged", "tiny", "all"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "hi", "hi_prefill", "prefill", "ragged", "tiny", "all"],
                     help="decode prints the metric line; the others print their own figures as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true", help="run a 1 GiB device copy first (PMC scaling)")
     args = ap.parse_args()
@@ -335,8 +390,11 @@ def main():
     if args.workload != "decode":
         extra = {}
         if args.workload in ("hi", "all"):
-            extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup,
-                                                 lengths=[int(v) for v in args.hi_lengths.split(",")])
+            hl = [int(v) for v in args.hi_lengths.split(",")]
+            extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup, lengths=hl)
+            extra["hi_decode_batch8_B8"] = bench_hi(args.steps, args.warmup, lengths=hl, B=8)
+        if args.workload in ("hi_prefill", "all"):
+            extra["hi_prefill_qlen2048_B8"] = bench_hi_prefill(args.steps, args.warmup)
         if args.workload in ("prefill", "all"):
             extra["chunked_prefill_cli"] = bench_prefill(args.steps, args.warmup)
         if args.workload in ("ragged", "all"):

@@ -99,6 +99,18 @@ int lsa_page_means(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_
                    hipStream_t stream);
 
 /*
+ * The per-step upkeep of the same cache ([paper] §3.3 "Design choices": the means are cached, so
+ * each decode step only refreshes what the new tokens change): after every sequence b has grown by
+ * n_new tokens (kv_off and sb_off already describe the new lengths L_b), rebuild the sub-blocks
+ * holding tokens [max(L_b - n_new, 0), L_b) of each sequence -- at most ceil(n_new / B) + 1 per
+ * sequence -- exactly as lsa_page_means would.  Rows of other sub-blocks are not touched.  The
+ * launch covers n_new tokens per sequence whatever the lengths, so a decode step (n_new = 1) costs
+ * one small launch.  Errors: LSA_ERR_INVALID for n_new < 1, a bad dtype or missing pointers.
+ */
+int lsa_page_means_append(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
+                          int32_t head_dim, int32_t B, int64_t n_new, void *k_mean, hipStream_t stream);
+
+/*
  * HI stage 1 ([paper] §3.3 "Block-level coarse filtering"; recall set [review] §2.3):
  *   page score  S(r, p) = sum_j w[r,j] * sum_{n in page p} ReLU(q_idx[r,j,:] . k_mean[sb_off[b]+n,:])
  *   for the causal pages p <= floor(t / P) (-inf for the others), then pages[r, :M] = the M best

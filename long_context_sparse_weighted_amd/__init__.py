@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "liblsa.so")
 LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = range(5)
 LSA_F32, LSA_BF16 = 0, 1
 
-SYMBOLS = ("lsa_index_score", "lsa_page_means", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
+SYMBOLS = ("lsa_index_score", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
            "lsa_topk_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
            "lsa_layer_workspace_size", "lsa_status_string", "lsa_last_error")
 
@@ -59,6 +59,7 @@ def lib():
         RP = ctypes.POINTER(Rows)
         L.lsa_index_score.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, I32, I32, P, I64, P]
         L.lsa_page_means.argtypes = [ctypes.c_int, I32, P, P, P, I32, I32, I64, I64, P, P]
+        L.lsa_page_means_append.argtypes = [ctypes.c_int, I32, P, P, P, I32, I32, I64, P, P]
         L.lsa_page_recall.argtypes = [ctypes.c_int, RP, P, P, P, P, I32, I32, I32, I32, I32, P, I64, P, P, SZ, P]
         L.lsa_page_recall_workspace_size.argtypes = [RP, I32, I32, ctypes.POINTER(SZ)]
         L.lsa_topk.argtypes = [I32, P, I64, I64, P, I32, I32, I32, P, P, SZ, P]
@@ -165,6 +166,16 @@ def lsa_page_means(kv_off, sb_off, k_idx, B, max_kv_len, k_mean=None, first_toke
         k_mean = torch.empty((int(sb_off[-1].item()), k_idx.shape[1]), dtype=k_idx.dtype, device=k_idx.device)
     _check(lib().lsa_page_means(_dt(k_idx), kv_off.numel() - 1, _p(kv_off), _p(sb_off), _p(k_idx), k_idx.shape[1],
                                 int(B), int(max_kv_len), int(first_token), _p(k_mean), _stream()))
+    return k_mean
+
+
+def lsa_page_means_append(kv_off, sb_off, k_idx, B, k_mean, n_new=1):
+    """Refresh, in place, the rows of k_mean for the sub-blocks holding each sequence's n_new newest
+    tokens (kv_off / sb_off describe the lengths after appending)."""
+    _need(kv_off, torch.int64, "kv_off")
+    _need(sb_off, torch.int64, "sb_off")
+    _check(lib().lsa_page_means_append(_dt(k_idx), kv_off.numel() - 1, _p(kv_off), _p(sb_off), _p(k_idx),
+                                       k_idx.shape[1], int(B), int(n_new), _p(k_mean), _stream()))
     return k_mean
 
 

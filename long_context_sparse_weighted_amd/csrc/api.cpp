@@ -252,9 +252,27 @@ int lsa_page_means(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_
         return fail(LSA_ERR_INVALID, "kv_off, sb_off, k_idx and k_mean must be device pointers");
     if (ceil_div(max_kv_len, B) * head_dim >= ((int64_t)1 << 31) * 256)
         return fail(LSA_ERR_UNSUPPORTED, "too many sub-blocks");
-    hipError_t e = launch_page_means(dtype, n_seq, kv_off, sb_off, k_idx, head_dim, B, max_kv_len, first_token, k_mean,
-                                     stream);
+    hipError_t e = launch_page_means(dtype, n_seq, kv_off, sb_off, k_idx, head_dim, B, max_kv_len, first_token, 0,
+                                     k_mean, stream);
     return hip_status(e, "lsa_page_means launch");
+}
+
+int lsa_page_means_append(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
+                          int32_t head_dim, int32_t B, int64_t n_new, void *k_mean, hipStream_t stream)
+{
+    if (dtype != LSA_F32 && dtype != LSA_BF16)
+        return fail(LSA_ERR_INVALID, "dtype must be LSA_F32 or LSA_BF16");
+    if (n_seq < 0 || head_dim <= 0 || B <= 0 || n_new < 1)
+        return fail(LSA_ERR_INVALID, "n_seq, head_dim, B, n_new out of range");
+    if (n_seq > kMaxGridRows)
+        return fail(LSA_ERR_UNSUPPORTED, "n_seq above %lld", (long long)kMaxGridRows);
+    if (n_seq > 0 && (!kv_off || !sb_off || !k_idx || !k_mean))
+        return fail(LSA_ERR_INVALID, "kv_off, sb_off, k_idx and k_mean must be device pointers");
+    if ((ceil_div(n_new, B) + 1) * head_dim >= ((int64_t)1 << 31) * 256)
+        return fail(LSA_ERR_UNSUPPORTED, "n_new too large (use lsa_page_means)");
+    // max_kv_len only gates the launch here: any value >= 1 lets every sequence through
+    hipError_t e = launch_page_means(dtype, n_seq, kv_off, sb_off, k_idx, head_dim, B, 1, 0, n_new, k_mean, stream);
+    return hip_status(e, "lsa_page_means_append launch");
 }
 
 int lsa_page_recall_workspace_size(const lsa_rows_t *rows, int32_t P, int32_t M, size_t *bytes)

@@ -335,7 +335,19 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             int grouped)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
-    const int r = blockIdx.y;
+    // Blocks go to the 8 XCDs in turn, in launch order (chunk fastest), so chunk c of every row lands
+    // on the XCD of c mod 8.  A paged row's chunks can differ a lot in work (a recall list that is
+    // mostly padding leaves its last chunks empty), so paged blocks are taken chunk by chunk instead,
+    // all rows of a chunk before the next chunk, with the rows rotated by the chunk index: the busy
+    // first chunks come first and are spread over every XCD, and the chunks of one row still land
+    // on different XCDs.
+    int r = blockIdx.y;
+    int64_t chunk = blockIdx.x;
+    if constexpr (MODE == kModePaged) {
+        const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        chunk = lin / gridDim.y;
+        r = (int)((lin % gridDim.y + chunk) % gridDim.y);
+    }
     if (row_mode && row_mode[r] != want)
         return;
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
@@ -349,16 +361,39 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     const int n = lane & 15;
     const int g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
-    const int64_t c_first = (int64_t)blockIdx.x * cols_per_block;
+    const int64_t c_first = chunk * cols_per_block;
     const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
     float *out = scores + (int64_t)r * ld;
-    // Columns of this chunk that can hold keys: [c_begin, c_end).  A flat column is a token position,
-    // so the chunk is cut to the row's range [lo, hi) (its start kept on a 64-column group); a paged
-    // column maps through the page list, and the whole chunk is kept.  The columns cut off are -inf.
+    // Columns of this chunk that can hold keys: [c_begin, c_end), the others are written -inf.  A flat
+    // column is a token position, so the chunk is cut to the row's range [lo, hi) (its start kept on
+    // a 64-column group); a paged column maps through the page list (see below).
     int64_t c_begin = c_first, c_end = c_last;
     if constexpr (MODE == kModeFlat) {
         c_begin = max(c_first, cm.lo / 64 * 64);
         c_end = min(c_last, cm.hi);
+    } else {
+        // Paged: the chunk is cut to the slots from the first to the last one whose page has keys in
+        // [lo, hi) (recall lists end in -1 padding, and pages past the middle range come last), so
+        // the unused slots of a short row stream nothing.
+        __shared__ int32_t slot_span[2];
+        if (threadIdx.x == 0)
+            slot_span[0] = INT32_MAX, slot_span[1] = -1;
+        __syncthreads();
+        const int32_t s_lo = (int32_t)(c_first / cm.P), s_hi = (int32_t)min<int64_t>((c_last + cm.P - 1) / cm.P, cm.M);
+        for (int32_t sl = s_lo + (int32_t)threadIdx.x; sl < s_hi; sl += (int32_t)blockDim.x) {
+            const int64_t pg = cm.page_row ? cm.page_row[sl] : -1;
+            if (pg >= 0 && pg * cm.P < cm.hi && (pg + 1) * cm.P > cm.lo) {
+                atomicMin(&slot_span[0], sl);
+                atomicMax(&slot_span[1], sl);
+            }
+        }
+        __syncthreads();
+        if (slot_span[1] < 0) {
+            c_begin = c_last;  // nothing to score
+        } else {
+            c_begin = max(c_first, (int64_t)slot_span[0] * cm.P / 64 * 64);
+            c_end = min(c_last, ((int64_t)slot_span[1] + 1) * cm.P);
+        }
     }
     if (cm.lo >= cm.hi || c_begin >= c_end) {  // no keys here (the DMAs below need a row of keys)
         for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)

@@ -36,8 +36,8 @@ hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len
 
 // --- sub-block means (hi.hip)
 hipError_t launch_page_means(int dtype, int n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
-                             int head_dim, int B, int64_t max_kv_len, int64_t first_token, void *k_mean,
-                             hipStream_t stream);
+                             int head_dim, int B, int64_t max_kv_len, int64_t first_token, int64_t n_new,
+                             void *k_mean, hipStream_t stream);
 
 // --- attention (attn.hip)
 size_t attn_workspace_bytes(int dtype, int n_rows, int n_heads, int d_v, int k_total);

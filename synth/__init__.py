@@ -142,7 +142,7 @@ def decode_batch(lengths, *, HI=64, dI=128, H=128, Dqk=576, Dv=512, k_sink=16, k
 
 def prefill_chunk(prefix, chunk, *, HI=64, dI=128, H=128, Dqk=576, Dv=512, k_sink=16, k_swa=1024,
                   k_sparse=1024, needles=0, dtype=torch.bfloat16, device="cuda", seed=0, with_attn=True,
-                  n_layers=1):
+                  n_layers=1, P=128, B=128, M=1024, hi_min_len=None):
     """One sequence of prefix+chunk tokens; the chunk's rows t = prefix .. prefix+chunk-1 attend causally.
     n_layers > 1 adds independent q / kv per extra (CLI reuse) layer."""
     g = generator(seed, device)
@@ -169,8 +169,9 @@ def prefill_chunk(prefix, chunk, *, HI=64, dI=128, H=128, Dqk=576, Dv=512, k_sin
             s = int(hrng.integers(mlo, mhi))
             plant_needle(k_idx, s, q_idx[r], w[r])
             needle_pos.append((r, s))
-    cfg = dict(HI=HI, dI=dI, H=H, Dqk=Dqk, Dv=Dv, scale=1.0 / math.sqrt(Dqk), P=128, B=128, M=1024,
-               hi_min_len=1 << 62, is_owner=1, **_budget(k_sink, k_swa, k_sparse))
+    cfg = dict(HI=HI, dI=dI, H=H, Dqk=Dqk, Dv=Dv, scale=1.0 / math.sqrt(Dqk), P=P, B=B, M=M,
+               hi_min_len=(1 << 62) if hi_min_len is None else int(hi_min_len), is_owner=1,
+               **_budget(k_sink, k_swa, k_sparse))
     return dict(cfg=cfg, kv_off=kv_off.to(device), kv_off_host=kv_off, row_seq=row_seq.to(device),
                 row_pos=row_pos.to(device), row_pos_host=row_pos, row_seq_host=row_seq, idx_row=None,
                 idx_row_host=None, q_idx=q_idx, w=w, k_idx=k_idx, q=layers[0][0] if layers else None,
@@ -235,3 +236,11 @@ def chunked_prefill_cli(device="cuda", seed=0, prefix=131072, chunk=8192, **kw):
     """An 8192-token causal chunk over a 131072-token prefix; owner layer (indexer + topK + attention)
     and one CLI reuse layer with independent q / kv."""
     return prefill_chunk(prefix, chunk, device=device, seed=seed, n_layers=2, **kw)
+
+
+def hi_prefill(L, device="cuda", seed=0, q_len=2048, **kw):
+    """Chunked prefill under Hierarchical Indexing: the last q_len rows of an L-token sequence, sub-block
+    B = 8, page P = 128, M = 1024 recalled pages (the HI-vs-flat prefill measurement of the pages:
+    q_len 2048, KV 32K .. 1M); independent Gaussian indexer inputs, no needles."""
+    kw.setdefault("with_attn", False)
+    return prefill_chunk(L - q_len, q_len, device=device, seed=seed, P=128, B=8, M=1024, hi_min_len=0, **kw)

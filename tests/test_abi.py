@@ -105,6 +105,11 @@ def test_page_validation(L):
     assert call(128, 128, 1024, ws=0) == L.LSA_ERR_WORKSPACE
     assert lib.lsa_page_means(1, 1, fake, fake, fake, 128, 0, 100, 0, fake, None) == L.LSA_ERR_INVALID
     assert lib.lsa_page_means(1, 1, fake, fake, fake, 128, 8, 100, -1, fake, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_page_means_append(1, 1, fake, fake, fake, 128, 8, 0, fake, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_page_means_append(1, 1, fake, fake, fake, 128, 0, 1, fake, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_page_means_append(2, 1, fake, fake, fake, 128, 8, 1, fake, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_page_means_append(1, 1, None, fake, fake, 128, 8, 1, fake, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_page_means_append(1, 0, None, None, None, 128, 8, 1, None, None) == L.LSA_OK  # nothing to do
 
 
 def test_attn_and_layer_validation(L):

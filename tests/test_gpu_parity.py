@@ -196,6 +196,29 @@ def test_page_means_bit_exact(dtype, B):
     assert np.array_equal(host(got2), want2)
 
 
+@pytest.mark.parametrize("dtype,B,n_new", [(torch.bfloat16, 8, 1), (torch.bfloat16, 8, 20), (torch.bfloat16, 128, 1),
+                                           (torch.float32, 16, 3)])
+def test_page_means_append_bit_exact(dtype, B, n_new):
+    # A decode step appended n_new tokens to every sequence: the sub-blocks holding them are rebuilt to
+    # the oracle's full-cache means; every other row of the cache is left as it was (here a sentinel).
+    lengths = [1, 8, 9, 127, 128, 129, 4999, 70000]
+    g = synth.generator(5, DEV)
+    kv_off = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]), dtype=torch.int64)
+    k = synth.normal((int(kv_off[-1]), 128), 1 / math.sqrt(128), g, DEV, dtype)
+    sb_off = lsa.sb_offsets(lengths, B)
+    want = ref.page_means(kv_off.numpy(), sb_off.numpy(), host(k), B)
+    touched = np.zeros(len(want), bool)
+    for b, L in enumerate(lengths):
+        first = max(L - n_new, 0)
+        touched[int(sb_off[b]) + first // B:int(sb_off[b + 1])] = True
+    stale = np.where(touched[:, None], np.zeros_like(want) + 7, np.zeros_like(want)).astype(want.dtype)
+    km = (synth.bits_to_bf16(stale) if dtype == torch.bfloat16 else torch.from_numpy(stale)).to(DEV)
+    lsa.lsa_page_means_append(kv_off.to(DEV), sb_off.to(DEV), k, B, km, n_new=n_new)
+    got = host(km)
+    assert np.array_equal(got[touched], want[touched])
+    assert np.array_equal(got[~touched], stale[~touched])
+
+
 # --------------------------------------------------------------------------------------------- a4/a5 HI
 
 
@@ -461,6 +484,33 @@ def test_layer_hi_vs_oracle(B):
     g_idx = host(idx)
     hits = sum(len(set(p) & set(g_idx[b].tolist())) for b, p in enumerate(x["needles"]))
     log(f"HI B={B}: needles picked {hits}/{sum(len(p) for p in x['needles'])}")
+
+
+def test_layer_hi_chunked_prefill_vs_oracle():
+    # HI on the rows of a prefill chunk with sub-blocks of 8: the page of row t also holds tokens after
+    # t, which lie in the window or in the future and never yield candidates.  The oracle runs on rows
+    # on both sides of the page edges crossed by the chunk (t = 38016 and 38144 start pages).
+    x = synth.prefill_chunk(38000, 160, device=DEV, seed=11, B=8, M=24, hi_min_len=0)
+    c = x["cfg"]
+    sb_off = lsa.sb_offsets(x["lengths"], c["B"])
+    km = lsa.lsa_page_means(x["kv_off"], sb_off.to(DEV), x["k_idx"], c["B"], x["max_len"])
+    o = oracle_inputs(x)
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], c["B"])
+    assert np.array_equal(host(km), km_o)
+    idx, out, lse = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"],
+                                      sb_off=sb_off.to(DEV), k_mean=km)
+    sel = np.array([0, 15, 16, 17, 80, 143, 144, 159])
+    os_ = dict(o)
+    for k in ("row_seq", "row_pos", "q_idx", "w", "q"):
+        os_[k] = o[k][sel]
+    w_idx, w_out, w_lse = ref.layer_fwd(c, os_["kv_off"], os_["row_seq"], os_["row_pos"], os_["q_idx"], os_["w"],
+                                        o["k_idx"], os_["q"], o["kv"], sb_off=sb_off.numpy(), k_mean=km_o)
+    _compare_layer(x, host(idx)[sel], host(out)[sel], host(lse)[sel], w_idx, w_out, w_lse, 2e-2,
+                   OracleRanking(os_, c, sb_off.numpy(), km_o))
+    # the recall restricts the candidates: the flat indexer picks differently on most rows
+    flat = lsa.lsa_layer_fwd(dict(c, hi_min_len=1 << 62), rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"],
+                             k_idx=x["k_idx"])[0]
+    assert (host(flat) != host(idx)).any(axis=1).mean() > 0.5
 
 
 def test_layer_hi_all_rows_bound():

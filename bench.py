@@ -156,6 +156,52 @@ def run_length(L, batch, steps, warmup, seed=0):
     return res
 
 
+def bench_fp8(steps, warmup, lengths=(131072, 1048576), batch=32):
+    """Decode step with the FP8 indexer (the decode batch of the headline, same inputs): per step the
+    queries are quantized, the FP8 key cache (quantized once, outside the step) is scored, then top-K
+    and the bf16 hybrid attention, all through the C ABI on one stream."""
+    import torch
+
+    import long_context_sparse_weighted_amd as lsa
+    import synth
+    res = {}
+    for L in lengths:
+        x = synth.decode_sweep(L, device="cuda", batch=batch)
+        c = x["cfg"]
+        bud = (c["k_sink"], c["k_swa"], c["k_sparse"])
+        rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"], L)
+        t_kq = time_on_stream(lambda: lsa.lsa_quantize_fp8(x["k_idx"]), 2, 1)
+        k8, ks = lsa.lsa_quantize_fp8(x["k_idx"])
+        q8 = torch.empty(x["q_idx"].shape, dtype=torch.uint8, device="cuda")
+        qs = torch.empty(x["q_idx"].shape[:2], dtype=torch.float32, device="cuda")
+        scores = torch.empty((batch, L), dtype=torch.float32, device="cuda")
+        idx = torch.empty((batch, c["k_sparse"]), dtype=torch.int32, device="cuda")
+        out = torch.empty((batch, c["H"], c["Dv"]), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((batch, c["H"]), dtype=torch.float32, device="cuda")
+
+        def step():
+            lsa.lsa_quantize_fp8(x["q_idx"], q8, qs)
+            lsa.lsa_index_score_fp8(rows, q8, qs, x["w"], k8, ks, bud, scores=scores)
+            lsa.lsa_topk(scores, c["k_sparse"], idx=idx)
+            lsa.lsa_hybrid_attn(rows, x["q"], x["kv"], c["Dv"], c["scale"], bud, idx, out=out, lse=lse)
+        t_step = time_on_stream(step, steps, warmup)
+        t_score = time_on_stream(lambda: lsa.lsa_index_score_fp8(rows, q8, qs, x["w"], k8, ks, bud, scores=scores),
+                                 steps, warmup)
+        got = idx.cpu().numpy()
+        recall = sum(len(set(p) & set(got[b].tolist())) for b, p in enumerate(x["needles"])) / max(
+            1, sum(len(p) for p in x["needles"]))
+        mid = L - c["k_sink"] - c["k_swa"]
+        k_bytes = batch * mid * 132                     # E4M3 codes + fp32 scale per key
+        res[str(L)] = dict(step_us=t_step * 1e6, score_kernel_us=t_score * 1e6, score_kernel_bytes=k_bytes,
+                           score_kernel_gbs=k_bytes / t_score / 1e9, key_cache_quantize_us=t_kq * 1e6,
+                           needle_recall=recall)
+        log(f"[bench] FP8 indexer L={L}: step {t_step * 1e6:.1f} us, FP8 scoring {t_score * 1e6:.1f} us = "
+            f"{k_bytes / t_score / 1e9:.0f} GB/s, key cache quantize {t_kq * 1e6:.0f} us, needle recall {recall:.3f}")
+        del x, k8, ks, scores
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(L=131072, rows=4, batch=32, seed=0):
     """The oracle on a bounded sample: `rows` of the 32 rows of the L-token decode batch, one thread
     per row; extrapolated to the whole batch at the same thread count."""
@@ -375,7 +421,7 @@ def main():
     ap.add_argument("--lengths", default="131072,1048576")
     ap.add_argument("--hi-lengths", default="262144,524288,1048576", help="KV lengths of the HI workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="decode", choices=["decode", "hi", "hi_prefill", "prefill", "ragged", "tiny", "all"],
+    ap.add_argument("--workload", default="decode", choices=["decode", "hi", "hi_prefill", "fp8", "prefill", "ragged", "tiny", "all"],
                     help="decode prints the metric line; the others print their own figures as one JSON line")
     ap.add_argument("--copy-calibration", action="store_true", help="run a 1 GiB device copy first (PMC scaling)")
     args = ap.parse_args()
@@ -393,6 +439,8 @@ def main():
             hl = [int(v) for v in args.hi_lengths.split(",")]
             extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup, lengths=hl)
             extra["hi_decode_batch8_B8"] = bench_hi(args.steps, args.warmup, lengths=hl, B=8)
+        if args.workload in ("fp8", "all"):
+            extra["fp8_indexer_decode"] = bench_fp8(args.steps, args.warmup)
         if args.workload in ("hi_prefill", "all"):
             extra["hi_prefill_qlen2048_B8"] = bench_hi_prefill(args.steps, args.warmup)
         if args.workload in ("prefill", "all"):

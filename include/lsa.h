@@ -86,6 +86,33 @@ int lsa_index_score(int dtype, const lsa_rows_t *rows, const void *q_idx, const 
                     int32_t P, float *scores, int64_t ld_scores, hipStream_t stream);
 
 /*
+ * FP8 form of the indexer inputs ([paper] §2.2 "Lightning Indexer": the indexer supports FP8
+ * computation; the format below is this library's reading).  For each of the n_vec vectors of x
+ * [n_vec, dim] (a key's d_I dims, or one query head): scale[v] = 2^e with e the smallest integer
+ * such that max|x[v, :]| <= 448 * 2^e (e = 0 for an all-zero vector), and codes[v, i] = the OCP FP8
+ * E4M3 code (bias 7, subnormals, no infinities) nearest to x[v, i] / 2^e, ties to the even code;
+ * -0 is stored as +0 and no code saturates.  x is bf16 (dtype LSA_BF16) or fp32; codes [n_vec, dim]
+ * uint8 and scale [n_vec] fp32 are device buffers owned by the caller.  1 <= dim <= 256.  A key
+ * cache is quantized once, as tokens are appended; queries once per step.
+ */
+int lsa_quantize_fp8(int dtype, int64_t n_vec, int32_t dim, const void *x, uint8_t *codes, float *scale,
+                     hipStream_t stream);
+
+/*
+ * Lightning-Indexer scores from FP8 inputs: Eq. 1 of lsa_index_score on the dequantized values
+ *     I(r, s) = sum_j w[r, j] * ReLU(q_scale[r, j] * k_scale[s] * (dec(q8[r, j, :]) . dec(k8[s, :])))
+ * with q8 [n_rows, n_heads, head_dim] / q_scale [n_rows, n_heads] and k8 [tokens, head_dim] /
+ * k_scale [tokens] as produced by lsa_quantize_fp8; every other argument, the flat and page-mapped
+ * column layouts, the -inf conventions and the errors are those of lsa_index_score.  Keys stream at
+ * 132 bytes each instead of 256.  Supported: (n_heads, head_dim) = (64, 128), on the CDNA4 FP8
+ * matrix instruction (products exact, sums in fp32).
+ */
+int lsa_index_score_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q_scale, const float *w,
+                        const uint8_t *k8, const float *k_scale, int32_t n_heads, int32_t head_dim,
+                        lsa_budget_t budget, const int32_t *pages, int32_t M, int32_t P, float *scores,
+                        int64_t ld_scores, hipStream_t stream);
+
+/*
  * Sub-block mean cache of the indexer keys ([paper] §3.3 "Design choices": precomputed once per
  * sequence and cached).  Sub-block n of sequence b covers tokens [nB, min((n+1)B, L_b)); row
  * sb_off[b] + n of k_mean [sb_off[n_seq], head_dim] receives the mean over the tokens present,

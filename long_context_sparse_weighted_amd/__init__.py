@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "liblsa.so")
 LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = range(5)
 LSA_F32, LSA_BF16 = 0, 1
 
-SYMBOLS = ("lsa_index_score", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
+SYMBOLS = ("lsa_index_score", "lsa_quantize_fp8", "lsa_index_score_fp8", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
            "lsa_topk_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
            "lsa_layer_workspace_size", "lsa_status_string", "lsa_last_error")
 
@@ -59,6 +59,8 @@ def lib():
         RP = ctypes.POINTER(Rows)
         L.lsa_index_score.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, I32, I32, P, I64, P]
         L.lsa_page_means.argtypes = [ctypes.c_int, I32, P, P, P, I32, I32, I64, I64, P, P]
+        L.lsa_quantize_fp8.argtypes = [ctypes.c_int, I64, I32, P, P, P, P]
+        L.lsa_index_score_fp8.argtypes = [RP, P, P, P, P, P, I32, I32, Budget, P, I32, I32, P, I64, P]
         L.lsa_page_means_append.argtypes = [ctypes.c_int, I32, P, P, P, I32, I32, I64, P, P]
         L.lsa_page_recall.argtypes = [ctypes.c_int, RP, P, P, P, P, I32, I32, I32, I32, I32, P, I64, P, P, SZ, P]
         L.lsa_page_recall_workspace_size.argtypes = [RP, I32, I32, ctypes.POINTER(SZ)]
@@ -155,6 +157,40 @@ def lsa_index_score(rows: RowsDesc, q_idx, w, k_idx, budget, scores=None, pages=
         scores = torch.empty((n_rows, ld), dtype=torch.float32, device=q_idx.device)
     _check(lib().lsa_index_score(dt, ctypes.byref(rows.c()), _p(q_idx), _p(w), _p(k_idx), HI, dI, Budget(*budget),
                                  _p(pages), int(M), int(P), _p(scores), int(ld), _stream()))
+    return scores
+
+
+def lsa_quantize_fp8(x, codes=None, scale=None):
+    """x [..., d] bf16 / fp32 -> (codes [..., d] uint8 E4M3, scale [...] fp32 powers of two)."""
+    d = x.shape[-1]
+    n_vec = x.numel() // d if d else 0
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib().lsa_quantize_fp8(_dt(x), n_vec, d, _p(x), _p(codes), _p(scale), _stream()))
+    return codes, scale
+
+
+def lsa_index_score_fp8(rows: RowsDesc, q8, q_scale, w, k8, k_scale, budget, scores=None, pages=None, M=0, P=0,
+                        ld=None):
+    """Eq. 1 scores [n_rows, ld] fp32 from FP8 indexer inputs (flat, or page-mapped with ``pages``)."""
+    n_rows, HI, dI = q8.shape
+    _need(q8, torch.uint8, "q8")
+    _need(k8, torch.uint8, "k8")
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (w, "w")):
+        _need(t, torch.float32, name)
+    if pages is not None:
+        _need(pages, torch.int32, "pages")
+        M = pages.shape[1]
+        ld = ld or M * P
+    else:
+        ld = ld or max(int(rows.max_kv_len), 1)
+    if scores is None:
+        scores = torch.empty((n_rows, ld), dtype=torch.float32, device=q8.device)
+    rc = rows.c()
+    _check(lib().lsa_index_score_fp8(ctypes.byref(rc), _p(q8), _p(q_scale), _p(w), _p(k8), _p(k_scale), HI, dI,
+                                     Budget(*budget), _p(pages), int(M), int(P), _p(scores), int(ld), _stream()))
     return scores
 
 

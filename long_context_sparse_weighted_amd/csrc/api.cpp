@@ -238,6 +238,57 @@ int lsa_index_score(int dtype, const lsa_rows_t *rows, const void *q_idx, const 
     return hip_status(e, "lsa_index_score launch");
 }
 
+int lsa_quantize_fp8(int dtype, int64_t n_vec, int32_t dim, const void *x, uint8_t *codes, float *scale,
+                     hipStream_t stream)
+{
+    if (dtype != LSA_F32 && dtype != LSA_BF16)
+        return fail(LSA_ERR_INVALID, "dtype must be LSA_F32 or LSA_BF16");
+    if (n_vec < 0 || dim < 1)
+        return fail(LSA_ERR_INVALID, "n_vec >= 0 and dim >= 1 required");
+    if (dim > 256)
+        return fail(LSA_ERR_UNSUPPORTED, "dim above 256");
+    if (n_vec >= ((int64_t)1 << 33))
+        return fail(LSA_ERR_UNSUPPORTED, "n_vec too large");
+    if (n_vec > 0 && (!x || !codes || !scale))
+        return fail(LSA_ERR_INVALID, "x, codes and scale must be device pointers");
+    hipError_t e = launch_quantize_fp8(dtype, n_vec, dim, x, codes, scale, stream);
+    return hip_status(e, "lsa_quantize_fp8 launch");
+}
+
+int lsa_index_score_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q_scale, const float *w,
+                        const uint8_t *k8, const float *k_scale, int32_t n_heads, int32_t head_dim,
+                        lsa_budget_t budget, const int32_t *pages, int32_t M, int32_t P, float *scores,
+                        int64_t ld_scores, hipStream_t stream)
+{
+    if (int st = check_rows(rows))
+        return st;
+    if (int st = check_budget(budget))
+        return st;
+    if (n_heads != 64 || head_dim != 128)
+        return fail(LSA_ERR_UNSUPPORTED, "FP8 indexer compiled for 64 heads of dim 128 only (got %d, %d)", n_heads,
+                    head_dim);
+    if (rows->n_rows > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !scores))
+        return fail(LSA_ERR_INVALID, "q8, q_scale, w, k8, k_scale and scores must be device pointers");
+    if (pages) {
+        if (M <= 0 || P <= 0)
+            return fail(LSA_ERR_INVALID, "page mode needs M > 0 and P > 0");
+        if (P % 16 != 0)
+            return fail(LSA_ERR_UNSUPPORTED, "page mode needs P %% 16 == 0");
+        if ((int64_t)M * P >= ((int64_t)1 << 31))
+            return fail(LSA_ERR_INVALID, "M*P overflows int32");
+        if (ld_scores < (int64_t)M * P)
+            return fail(LSA_ERR_INVALID, "ld_scores %lld < M*P", (long long)ld_scores);
+    } else if (ld_scores < rows->max_kv_len) {
+        return fail(LSA_ERR_INVALID, "ld_scores %lld < max_kv_len %lld", (long long)ld_scores,
+                    (long long)rows->max_kv_len);
+    }
+    if (ld_scores >= ((int64_t)1 << 31))
+        return fail(LSA_ERR_UNSUPPORTED, "ld_scores must be below 2^31");
+    hipError_t e = launch_index_score_fp8(to_dev(rows), q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, pages,
+                                          M, P, scores, ld_scores, stream);
+    return hip_status(e, "lsa_index_score_fp8 launch");
+}
+
 int lsa_page_means(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
                    int32_t head_dim, int32_t B, int64_t max_kv_len, int64_t first_token, void *k_mean,
                    hipStream_t stream)

@@ -292,8 +292,14 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uin
 // tiles k + 1 .. k + S - 1 follow its own; score stores in between only make "at most 4 (S - 1)
 // outstanding" stricter.
 
+// Two blocks per CU, each wave with a 4-deep ring (64 KB of LDS per block): two waves per SIMD then
+// overlap one wave's DMA issue with the other's products (decode 32 x 128K: 188 us against 199 us
+// with one block of 6-deep rings; 32 x 1M: 1479 against 1511 us).
 #ifndef LSA_SCORE_RING
-#define LSA_SCORE_RING 6
+#define LSA_SCORE_RING 4
+#endif
+#ifndef LSA_SCORE_BLOCKS_PER_CU
+#define LSA_SCORE_BLOCKS_PER_CU 2
 #endif
 constexpr int kScoreRing = LSA_SCORE_RING;
 
@@ -325,56 +331,40 @@ __device__ inline void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int MODE, int S>
-__global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
-                                                            const float *__restrict__ w,
-                                                            const uint16_t *__restrict__ keys, int k_sink, int k_swa,
-                                                            const int32_t *__restrict__ pages, int M, int P,
-                                                            float *__restrict__ scores, int64_t ld, int64_t n_cols,
-                                                            int64_t cols_per_block, const uint8_t *row_mode, int want,
-                                                            int grouped)
+// Block -> (row, chunk) of the streaming kernels.  Blocks go to the 8 XCDs in turn, in launch order
+// (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  A paged row's chunks can
+// differ a lot in work (a recall list that is mostly padding leaves its last chunks empty), so paged
+// blocks are taken chunk by chunk instead, all rows of a chunk before the next chunk, with the rows
+// rotated by the chunk index: the busy first chunks come first and are spread over every XCD, and
+// the chunks of one row still land on different XCDs.
+template <int MODE>
+__device__ inline void stream_block(int &r, int64_t &chunk)
 {
-    static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
-    // Blocks go to the 8 XCDs in turn, in launch order (chunk fastest), so chunk c of every row lands
-    // on the XCD of c mod 8.  A paged row's chunks can differ a lot in work (a recall list that is
-    // mostly padding leaves its last chunks empty), so paged blocks are taken chunk by chunk instead,
-    // all rows of a chunk before the next chunk, with the rows rotated by the chunk index: the busy
-    // first chunks come first and are spread over every XCD, and the chunks of one row still land
-    // on different XCDs.
-    int r = blockIdx.y;
-    int64_t chunk = blockIdx.x;
+    r = blockIdx.y;
+    chunk = blockIdx.x;
     if constexpr (MODE == kModePaged) {
         const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
         chunk = lin / gridDim.y;
         r = (int)((lin % gridDim.y + chunk) % gridDim.y);
     }
-    if (row_mode && row_mode[r] != want)
-        return;
-    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
-        return;  // scored by the multi-row kernel
-    __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
-    const RowInfo ri = row_info(rows, r);
-    const SiRanges si = si_ranges(ri, k_sink, k_swa);
-    const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
+}
 
-    const int lane = lane_id();
-    const int n = lane & 15;
-    const int g = lane >> 4;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
-    const int64_t c_first = chunk * cols_per_block;
-    const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
-    float *out = scores + (int64_t)r * ld;
-    // Columns of this chunk that can hold keys: [c_begin, c_end), the others are written -inf.  A flat
-    // column is a token position, so the chunk is cut to the row's range [lo, hi) (its start kept on
-    // a 64-column group); a paged column maps through the page list (see below).
-    int64_t c_begin = c_first, c_end = c_last;
+// Columns of the chunk [c_first, c_last) that can hold keys: [c_begin, c_end) (empty when
+// c_begin >= c_end).  A flat column is a token position, so the chunk is cut to the row's range
+// [lo, hi) (its start kept on a 64-column group).  A paged chunk is cut to the slots from the first
+// to the last one whose page has keys in [lo, hi) (recall lists end in -1 padding, and pages past
+// the middle range come last), so the unused slots of a short row stream nothing.  Every thread of
+// the block calls it (paged: two barriers).
+template <int MODE>
+__device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_t c_last, int64_t &c_begin,
+                                       int64_t &c_end)
+{
+    c_begin = c_first;
+    c_end = c_last;
     if constexpr (MODE == kModeFlat) {
         c_begin = max(c_first, cm.lo / 64 * 64);
         c_end = min(c_last, cm.hi);
     } else {
-        // Paged: the chunk is cut to the slots from the first to the last one whose page has keys in
-        // [lo, hi) (recall lists end in -1 padding, and pages past the middle range come last), so
-        // the unused slots of a short row stream nothing.
         __shared__ int32_t slot_span[2];
         if (threadIdx.x == 0)
             slot_span[0] = INT32_MAX, slot_span[1] = -1;
@@ -395,6 +385,40 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             c_end = min(c_last, ((int64_t)slot_span[1] + 1) * cm.P);
         }
     }
+}
+
+template <int MODE, int S>
+__global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
+                                                            const float *__restrict__ w,
+                                                            const uint16_t *__restrict__ keys, int k_sink, int k_swa,
+                                                            const int32_t *__restrict__ pages, int M, int P,
+                                                            float *__restrict__ scores, int64_t ld, int64_t n_cols,
+                                                            int64_t cols_per_block, const uint8_t *row_mode, int want,
+                                                            int grouped)
+{
+    static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
+    int r;
+    int64_t chunk;
+    stream_block<MODE>(r, chunk);
+    if (row_mode && row_mode[r] != want)
+        return;
+    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
+        return;  // scored by the multi-row kernel
+    __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges si = si_ranges(ri, k_sink, k_swa);
+    const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
+
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
+    const int64_t c_first = chunk * cols_per_block;
+    const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
+    float *out = scores + (int64_t)r * ld;
+    // Columns of this chunk that can hold keys: [c_begin, c_end); the others are written -inf.
+    int64_t c_begin, c_end;
+    chunk_key_range<MODE>(cm, c_first, c_last, c_begin, c_end);
     if (cm.lo >= cm.hi || c_begin >= c_end) {  // no keys here (the DMAs below need a row of keys)
         for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
@@ -557,6 +581,232 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
     }
 }
+
+// ------------------------------------------------------------------------------------------
+// FP8 streaming kernel: the same per-row work with E4M3 codes (128 B per key, one power-of-two scale
+// per key and per query head), on the CDNA4 FP8 matrix instruction v_mfma_scale_f32_16x16x128_f8f6f4
+// (both operands E4M3, unit block scales).  One 16x16x128 product covers a head block's whole dot
+// product, so a 16-key tile takes 4 of them.  Since the key scale is positive,
+//     sum_j w_j ReLU(sq_j sk q8_j . k8) = sk * sum_j (w_j sq_j) ReLU(q8_j . k8):
+// the query scales fold into the head weights and the key scale multiplies the sum.
+//
+// A tile (16 keys) arrives by three DMA instructions into a 2304-byte ring slot: two of 1 KB for the
+// codes (8 keys each) and one global_load_lds_dword for the 16 key scales (lane l fetches the scale
+// of key l % 16, so each is stored four times).  16-byte chunk c of key k sits at chunk slot
+// 8 k + (c ^ ((k >> 1) & 7)): the 16 lanes reading chunk c of keys 0..15 hit 16 different 16-byte
+// bank groups.  Each step issues exactly 3 DMA instructions, and the waits count them.
+
+// A tile of FP8 keys is half the bytes of a bf16 tile for about the same per-tile instruction work,
+// so one wave per SIMD cannot keep enough of them moving: the grid is sized for two blocks per CU
+// (decode 32 x 128K: 100 us against 153 us with one), each with a 4-deep ring (37 KB of LDS).
+#ifndef LSA_FP8_BLOCKS_PER_CU
+#define LSA_FP8_BLOCKS_PER_CU 2
+#endif
+#ifndef LSA_FP8_RING
+#define LSA_FP8_RING 4
+#endif
+constexpr int kFp8Ring = LSA_FP8_RING;
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+constexpr int kDim8 = 128;                          // bytes per key (E4M3 codes of d_I = 128)
+constexpr int kTileCodes8 = kTile * kDim8;          // 2 KB
+constexpr int kSlot8 = kTileCodes8 + 64 * 4;        // + the scale copies
+
+__device__ inline void dma_4s(const void *sbase, uint32_t voff, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 " LSA_DMA_CPOL ::"v"(voff),
+                 "s"(sbase), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ inline void dma_4(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off " LSA_DMA_CPOL ::"v"(src),
+                 "s"(lds_base)
+                 : "memory", "m0");
+}
+
+template <int MODE, int S>
+__global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
+                                                         const float *__restrict__ q_scale,
+                                                         const float *__restrict__ w, const uint8_t *__restrict__ k8,
+                                                         const float *__restrict__ k_scale, int k_sink, int k_swa,
+                                                         const int32_t *__restrict__ pages, int M, int P,
+                                                         float *__restrict__ scores, int64_t ld, int64_t n_cols,
+                                                         int64_t cols_per_block)
+{
+    static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
+    int r;
+    int64_t chunk;
+    stream_block<MODE>(r, chunk);
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges si = si_ranges(ri, k_sink, k_swa);
+    const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
+
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c_first = chunk * cols_per_block;
+    const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
+    float *out = scores + (int64_t)r * ld;
+    int64_t c_begin, c_end;
+    chunk_key_range<MODE>(cm, c_first, c_last, c_begin, c_end);
+    if (cm.lo >= cm.hi || c_begin >= c_end) {
+        for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
+            out[c] = -INFINITY;
+        return;
+    }
+    for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
+        out[c] = -INFINITY;
+    for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
+        out[c] = -INFINITY;
+    // A operand of head block mt: lane (n, g) holds bytes 32 g .. 32 g + 31 of head 16 mt + n; the key
+    // operand uses the same byte split, so the product is the full 128-byte dot product.
+    i32x8 qa[4];
+    const uint8_t *qrow = q8 + (int64_t)r * kHeads * kDim8;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+        qa[mt] = *reinterpret_cast<const i32x8 *>(qrow + (mt * 16 + n) * kDim8 + 32 * g);
+    float wv[4][4];  // w * q scale of head 16 mt + 4 g + i
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(q_scale + (int64_t)r * kHeads + mt * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            wv[mt][i] = a[i] * b[i];
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        loaded_here(qa[mt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            loaded_here(wv[mt][i]);
+    }
+
+    constexpr int W = kWavesPerBlock;
+    const int64_t chunk_tile = c_begin / kTile;
+    const int64_t end_tile = (c_end + kTile - 1) / kTile;
+    const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
+    const int64_t K = wave < n_groups ? 4 * ((n_groups - wave + W - 1) / W) : 0;
+    auto tile_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
+        return chunk_tile + 4 * ((k >> 2) * W + wave) + (k & 3);
+    };
+    const int64_t safe_key = cm.base + cm.lo;
+    const uint32_t ring_base =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)&ring[0][wave][0];
+    constexpr uint32_t kRingStep = kWavesPerBlock * kSlot8;
+    auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
+        const int64_t c0 = tile * kTile;
+        if constexpr (MODE == kModeFlat) {
+            return c0;
+        } else {
+            const int slot = __builtin_amdgcn_readfirstlane((int)page_slot(cm, (uint32_t)c0));
+            if (slot >= cm.M)
+                return -1;
+            const int64_t pg = pages[(int64_t)r * M + slot];
+            return pg < 0 ? -1 : pg * cm.P + (c0 - (int64_t)slot * cm.P);
+        }
+    };
+    auto key_of = [&](int64_t tp, int i) __attribute__((always_inline)) -> int64_t {
+        const int64_t sp = tp + i;
+        return (tp >= 0 && sp >= cm.lo && sp < cm.hi) ? cm.base + sp : -1;
+    };
+    auto interior = [&](int64_t tp) __attribute__((always_inline)) {
+        return tp >= cm.lo && tp + kTile <= cm.hi;
+    };
+    // Code DMA j of a tile: lane l fetches chunk (l % 8) ^ ((k >> 1) & 7) of key k = 8 j + l / 8
+    // (byte offset from the tile's first key); the scale DMA: key l % 16.
+    uint32_t lane_off[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int kk = 8 * j + (lane >> 3);
+        lane_off[j] = (uint32_t)(kk * kDim8 + (((lane & 7) ^ ((kk >> 1) & 7)) * 16));
+    }
+    const uint32_t scale_off = (uint32_t)(n * 4);
+    auto issue = [&](int64_t k) __attribute__((always_inline)) {
+        const int64_t tile = min(tile_of(k < K ? k : K - 1), end_tile - 1);
+        const int64_t tp = tile_pos(tile);
+        const uint32_t buf = ring_base + (uint32_t)(k % S) * kRingStep;
+        if (interior(tp)) {
+            const uint8_t *kb = k8 + (cm.base + tp) * kDim8;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                dma_16s(kb, lane_off[j], buf + j * 1024);
+            dma_4s(k_scale + cm.base + tp, scale_off, buf + kTileCodes8);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int kk = 8 * j + (lane >> 3);
+                const int64_t key = key_of(tp, kk);
+                const int64_t row_k = key >= 0 ? key : safe_key;
+                dma_16(k8 + row_k * kDim8 + (((lane & 7) ^ ((kk >> 1) & 7)) * 16), buf + j * 1024);
+            }
+            const int64_t key = key_of(tp, n);
+            dma_4(k_scale + (key >= 0 ? key : safe_key), buf + kTileCodes8);
+        }
+    };
+    auto score_tile = [&](int64_t k, int64_t tp) __attribute__((always_inline)) -> float {
+        wait_vmcnt<3 * (S - 1)>();  // DMA(k) has landed: only DMA(k + 1 .. k + S - 1) may follow it
+        const bool any = interior(tp) || __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
+        u32x4 b0 = u32x4{0u, 0u, 0u, 0u}, b1 = b0;
+        float sk = 0.0f;
+        if (any) {
+            const uint8_t *slot = &ring[k % S][wave][0];
+            const int f = (n >> 1) & 7;
+            b0 = *reinterpret_cast<const u32x4 *>(slot + 16 * (8 * n + ((2 * g) ^ f)));
+            b1 = *reinterpret_cast<const u32x4 *>(slot + 16 * (8 * n + ((2 * g + 1) ^ f)));
+            sk = *reinterpret_cast<const float *>(slot + kTileCodes8 + 4 * n);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot k % S is free again
+        issue(k + S);
+        float v = 0.0f;
+        if (any) {
+            const i32x8 bb = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+            f32x4 acc[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], bb, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                           0, 0, 0, 127, 0, 127);
+            // acc[mt][i] = q8(head 16 mt + 4 g + i) . k8(key n)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v += wv[mt][i] * relu(acc[mt][i]);
+            v = sum_xor32(sum_xor16(v)) * sk;
+        }
+        return v;
+    };
+    if (K > 0) {
+        for (int k = 0; k < S; ++k)
+            issue(k);
+        for (int64_t k0 = 0; k0 < K; k0 += 4) {
+            const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
+            const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
+            const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
+            const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
+            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+            const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
+            const int64_t c = tile_of(k0 + g) * kTile + n;
+            const bool valid = key_of(tp, n) >= 0;
+            if (c < c_end)
+                out[c] = valid ? v : -INFINITY;
+        }
+        wait_vmcnt<0>();
+    }
+}
+
+// (explicit instantiations: without them the host stub of the flat kernel is not emitted)
+template __global__ void score_fp8_kernel<kModeFlat, kFp8Ring>(RowsDev, const uint8_t *, const float *, const float *,
+                                                                 const uint8_t *, const float *, int, int,
+                                                                 const int32_t *, int, int, float *, int64_t, int64_t,
+                                                                 int64_t);
+template __global__ void score_fp8_kernel<kModePaged, kFp8Ring>(RowsDev, const uint8_t *, const float *, const float *,
+                                                                  const uint8_t *, const float *, int, int,
+                                                                  const int32_t *, int, int, float *, int64_t, int64_t,
+                                                                  int64_t);
 
 // ------------------------------------------------------------------------------------------
 // Multi-row bf16 kernel (prefill): the 16 rows of a group share every key tile, so the keys are read
@@ -807,6 +1057,71 @@ __global__ __launch_bounds__(256) void score_valu_kernel(RowsDev rows, const flo
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// FP8 quantizer of the indexer inputs: per vector (a key's d_I dims, or one query head) the scale is
+// 2^e with e the smallest integer such that max|x| <= 448 * 2^e (e = 0 for an all-zero vector); each
+// element becomes the E4M3 code nearest to x / 2^e, ties to the even code (no saturation is ever
+// needed).  The scaling and the rounding are exact power-of-two operations and one round-to-nearest-
+// even, so the codes are bit for bit those of the definition.
+
+// E4M3 code of y, |y| <= 448: the grid quantum at |y| is 2^(E-3) for |y| in [2^E, 2^(E+1)), E >= -6,
+// and 2^-9 below 2^-6 (subnormals).
+__device__ inline uint32_t e4m3_code(float y)
+{
+    const float a = fabsf(y);
+    int ex;
+    (void)frexpf(a, &ex);          // a = f 2^ex, f in [0.5, 1)
+    int E = max(ex - 1, -6);
+    int nn = (int)rintf(ldexpf(a, 3 - E));  // units of the quantum, rounded to even; 0 .. 16
+    if (nn >= 16) {                // the rounding carried into the next binade
+        E += 1;
+        nn >>= 1;
+    }
+    uint32_t code = nn >= 8 ? (uint32_t)(((E + 7) << 3) | (nn - 8)) : (uint32_t)nn;
+    if (signbit(y) && code != 0u)
+        code |= 0x80u;
+    return code;
+}
+
+template <typename T>
+__device__ inline float load_as_float(const T *p);
+template <>
+__device__ inline float load_as_float<float>(const float *p) { return *p; }
+template <>
+__device__ inline float load_as_float<uint16_t>(const uint16_t *p) { return bf16_bits_to_float(*p); }
+
+// One wave per vector (dim <= 256: element lane + 64 i in the lane's register i).
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const T *__restrict__ x, int64_t n_vec, int dim,
+                                                            uint8_t *__restrict__ codes, float *__restrict__ scale)
+{
+    const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (v >= n_vec)
+        return;  // wave-uniform
+    const int lane = lane_id();
+    const T *xv = x + v * dim;
+    float e[4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = lane + 64 * i;
+        e[i] = idx < dim ? load_as_float<T>(xv + idx) : 0.0f;
+        amax = fmaxf(amax, fabsf(e[i]));
+    }
+    amax = wave_max(amax);
+    int ex;
+    const float f = frexpf(amax, &ex);  // amax = f 2^ex; 448 = 0.875 2^9
+    const int sexp = amax == 0.0f ? 0 : ex - 9 + (f > 0.875f ? 1 : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = lane + 64 * i;
+        if (idx < dim)
+            codes[v * dim + idx] = (uint8_t)e4m3_code(ldexpf(e[i], -sexp));
+    }
+    if (lane == 0)
+        scale[v] = ldexpf(1.0f, sexp);
+}
+
 // ------------------------------------------------------------------------------------------ host
 
 bool index_score_supported(int dtype, int n_heads, int head_dim)
@@ -822,9 +1137,9 @@ struct ScoreGeom {
     int n_chunks;
 };
 
-static ScoreGeom score_geometry(int64_t n_rows, int64_t n_cols)
+static ScoreGeom score_geometry(int64_t n_rows, int64_t n_cols, int blocks_per_cu = 1)
 {
-    int64_t cpb = n_rows * n_cols / 256;  // large blocks amortise the ring ramp-up and the Q / w loads
+    int64_t cpb = n_rows * n_cols / (256 * blocks_per_cu);  // large blocks amortise the ring ramp-up and the Q / w loads
     cpb = (cpb + 63) / 64 * 64;
     if (cpb < 256)
         cpb = 256;
@@ -850,15 +1165,18 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
                                w, (const uint16_t *)keys, k_sink, k_swa, scores, ld, n_cols, geo.chunk_elems,
                                gate.row_mode, gate.want);
         }
-        dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
-        if constexpr (MODE == kModePageMean)
+        if constexpr (MODE == kModePageMean) {
+            dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
             hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
                                (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
                                geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
-        else
+        } else {
+            const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
+            dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
             hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
-                               ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
+                               ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
+        }
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
         dim3 grid((unsigned)((threads_cols + 255) / 256), (unsigned)rows.n_rows);
@@ -896,6 +1214,38 @@ hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len
     // Sub-block columns: ld_ps pages x G sub-blocks, so every page column is produced by one tile.
     return launch_mode<kModePageMean>(dtype, rows, q_idx, w, k_mean, n_heads, head_dim, 0, 0, sb_off, nullptr, 0, P,
                                       B, page_scores, ld_ps, ld_ps * G, gate, stream);
+}
+
+hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,
+                                  const uint8_t *k8, const float *k_scale, int k_sink, int k_swa,
+                                  const int32_t *pages, int M, int P, float *scores, int64_t ld, hipStream_t stream)
+{
+    if (rows.n_rows == 0 || ld == 0)
+        return hipSuccess;
+    const ScoreGeom geo = score_geometry(rows.n_rows, ld, LSA_FP8_BLOCKS_PER_CU);
+    dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
+    if (pages)
+        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring>), grid, dim3(256), 0, stream, rows, q8, q_scale, w,
+                           k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems);
+    else
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring>), grid, dim3(256), 0, stream, rows, q8, q_scale, w,
+                           k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(int dtype, int64_t n_vec, int dim, const void *x, uint8_t *codes, float *scale,
+                               hipStream_t stream)
+{
+    if (n_vec == 0)
+        return hipSuccess;
+    dim3 grid((unsigned)((n_vec + 3) / 4));
+    if (dtype == 1)
+        hipLaunchKernelGGL(quantize_fp8_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t *)x, n_vec, dim,
+                           codes, scale);
+    else
+        hipLaunchKernelGGL(quantize_fp8_kernel<float>, grid, dim3(256), 0, stream, (const float *)x, n_vec, dim, codes,
+                           scale);
+    return hipGetLastError();
 }
 
 }  // namespace lsa

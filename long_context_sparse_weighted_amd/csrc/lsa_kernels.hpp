@@ -34,6 +34,13 @@ hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len
                               const void *q_idx, const float *w, const void *k_mean, int n_heads, int head_dim,
                               int P, int B, float *page_scores, int64_t ld_ps, RowGate gate, hipStream_t stream);
 
+// --- FP8 indexer (index_score.hip): E4M3 codes, one power-of-two scale per vector
+hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,
+                                  const uint8_t *k8, const float *k_scale, int k_sink, int k_swa,
+                                  const int32_t *pages, int M, int P, float *scores, int64_t ld, hipStream_t stream);
+hipError_t launch_quantize_fp8(int dtype, int64_t n_vec, int dim, const void *x, uint8_t *codes, float *scale,
+                               hipStream_t stream);
+
 // --- sub-block means (hi.hip)
 hipError_t launch_page_means(int dtype, int n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
                              int head_dim, int B, int64_t max_kv_len, int64_t first_token, int64_t n_new,

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     text = open(os.path.join(ROOT, "include", "lsa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lsa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -110,6 +110,30 @@ def test_page_validation(L):
     assert lib.lsa_page_means_append(2, 1, fake, fake, fake, 128, 8, 1, fake, None) == L.LSA_ERR_INVALID
     assert lib.lsa_page_means_append(1, 1, None, fake, fake, 128, 8, 1, fake, None) == L.LSA_ERR_INVALID
     assert lib.lsa_page_means_append(1, 0, None, None, None, 128, 8, 1, None, None) == L.LSA_OK  # nothing to do
+
+
+def test_fp8_validation(L):
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    q = lambda dt, n, d, x=fake: lib.lsa_quantize_fp8(dt, n, d, x, fake, fake, None)
+    assert q(2, 10, 128) == L.LSA_ERR_INVALID          # dtype
+    assert q(1, 10, 0) == L.LSA_ERR_INVALID            # dim
+    assert q(1, -1, 128) == L.LSA_ERR_INVALID
+    assert q(1, 10, 300) == L.LSA_ERR_UNSUPPORTED      # dim above 256
+    assert q(1, 10, 128, None) == L.LSA_ERR_INVALID    # missing buffer
+    assert q(1, 0, 128, None) == L.LSA_OK              # nothing to do
+    b = L.Budget(16, 1024, 1024)
+    r = _rows(L)
+    s = lambda H, D, ld, pages=None, M=0, P=0, k8=fake: lib.lsa_index_score_fp8(
+        ctypes.byref(r), fake, fake, fake, k8, fake, H, D, b, pages, M, P, fake, ld, None)
+    assert s(32, 128, 100) == L.LSA_ERR_UNSUPPORTED    # 64 heads of dim 128 only
+    assert s(64, 64, 100) == L.LSA_ERR_UNSUPPORTED
+    assert s(64, 128, 99) == L.LSA_ERR_INVALID         # ld below max_kv_len
+    assert s(64, 128, 100, k8=None) == L.LSA_ERR_INVALID
+    assert s(64, 128, 2048, fake, 16, 100) == L.LSA_ERR_UNSUPPORTED   # P % 16
+    assert s(64, 128, 1000, fake, 16, 128) == L.LSA_ERR_INVALID       # ld < M*P
+    assert lib.lsa_index_score_fp8(None, fake, fake, fake, fake, fake, 64, 128, b, None, 0, 0, fake, 100,
+                                   None) == L.LSA_ERR_INVALID
 
 
 def test_attn_and_layer_validation(L):

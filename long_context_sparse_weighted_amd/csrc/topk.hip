@@ -4,10 +4,12 @@
 // Keys are the order-preserving 32-bit images of the scores (-0 folded onto +0); -inf and NaN are
 // not candidates and map to key 0.  The selection runs in levels.  A block of 512 threads holds a
 // segment of 16384 keys in registers (thread t holds positions 32 t .. 32 t + 31 of the segment; a
-// whole row of at most 4096 columns goes to one block of 256 threads x 16 keys) and picks
-// its best k under (key desc, position asc) by MSB-first radix select: three digits (bits 31..21,
-// 20..10, 9..0), each counted in an LDS histogram whose suffix sums locate the bin of the k-th key;
-// keys above that bin are picked and, once all 32 bits are fixed, ties take the lowest positions.
+// whole row of at most 4096 columns goes to one block of 256 threads x 16 keys, a final list of at
+// most 8192 candidates to 512 threads x 16) and picks its best k under (key desc, position asc) by
+// MSB-first radix select.  The bits the block's smallest and largest candidates share are fixed at
+// once (every candidate shares them); the rest are taken in digits of at most 11 bits, each counted
+// in an LDS histogram whose suffix sums locate the bin of the k-th key; keys above that bin are
+// picked and, once all 32 bits are fixed, ties take the lowest positions.
 // The picks are written in position order.  The first level cuts each row into segments of 16384
 // scores and writes every segment's picks as a candidate list (key, position): the row's top k is
 // among them, since an element with fewer than k better elements in its row has fewer than k
@@ -21,8 +23,7 @@ namespace lsa {
 
 constexpr int kBins = 2048;
 
-__host__ __device__ inline int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
-__host__ __device__ inline int digit_width(int pass) { return pass == 2 ? 10 : 11; }
+constexpr int kDigitBits = 11;  // digits of at most 11 bits: 2048 bins
 
 #ifndef LSA_TOPK_THREADS
 #define LSA_TOPK_THREADS 512
@@ -32,6 +33,7 @@ constexpr int kSegThreads = LSA_TOPK_THREADS;
 constexpr int kVpt = kSeg / kSegThreads;        // keys per thread
 constexpr int kSmallThreads = 256;
 constexpr int kSmallVpt = 16;                   // a row of at most 4096 columns: one block of 256 x 16
+constexpr int kFinalVpt = 16;                   // a final candidate list of at most 8192: 512 x 16
 constexpr int kMaxLocalK = 4096;
 
 // Exclusive prefix sums over threads (in thread order) of two counters, and their totals.
@@ -55,6 +57,54 @@ __device__ __attribute__((always_inline)) inline void block_scan2(uint32_t a, ui
         sa += xa, sb += xb;
     }
     ea = pa + ia - a, eb = pb + ib - b, ta = sa, tb = sb;
+    __syncthreads();
+}
+
+// Inclusive wave min / max by the same DPP row shifts and broadcasts as wave_incl_scan (lane 63 ends
+// with the whole wave's); lanes without a source take the identity.
+__device__ inline uint32_t wave_incl_min(uint32_t v)
+{
+    constexpr int kId = -1;  // 0xffffffff
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x111, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x112, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x114, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x118, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x142, 0xa, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+__device__ inline uint32_t wave_incl_max(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+// Block totals of a count, and the min / max of the keys (scratch: 3 * NT / 64 words of LDS).
+template <int NT>
+__device__ __attribute__((always_inline)) inline void block_reduce3(uint32_t &cnt, uint32_t &kmin, uint32_t &kmax,
+                                                                    uint32_t *scratch)
+{
+    constexpr int NW = NT / kWave;
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    const uint32_t ic = wave_incl_scan(cnt);
+    kmin = wave_incl_min(kmin);
+    kmax = wave_incl_max(kmax);
+    if (lane == kWave - 1)
+        scratch[w] = ic, scratch[NW + w] = kmin, scratch[2 * NW + w] = kmax;
+    __syncthreads();
+    uint32_t c = 0, lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        c += scratch[i];
+        lo = min(lo, scratch[NW + i]);
+        hi = max(hi, scratch[2 * NW + i]);
+    }
+    cnt = c, kmin = lo, kmax = hi;
     __syncthreads();
 }
 
@@ -82,16 +132,26 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
                                                                  uint32_t *s_above, uint32_t *s_bin)
 {
     Selection sel{0u, 0, k, false, false};
-    uint32_t cnt = 0;
+    uint32_t total = 0, kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-    for (int m = 0; m < VPT; ++m)
-        cnt += key[m] != 0 ? 1u : 0u;
-    uint32_t e0, e1, total, t1;
-    block_scan2<NT>(cnt, 0, e0, e1, total, t1, scratch);
+    for (int m = 0; m < VPT; ++m) {
+        const uint32_t x = key[m];
+        total += x != 0 ? 1u : 0u;
+        kmin = min(kmin, x != 0 ? x : 0xffffffffu);
+        kmax = max(kmax, x);
+    }
+    block_reduce3<NT>(total, kmin, kmax, scratch);
     if (total <= k) {
         sel.all = true;
         return sel;
     }
+    // Every candidate lies in [kmin, kmax], so it shares their common leading bits: the digits start
+    // below them.  (The candidates of a later level, the best keys of their segments, sit in a narrow
+    // range whose fixed top digits would pile them into a few bins.)
+    sel.consumed = kmin == kmax ? 32 : __clz(kmin ^ kmax);
+    sel.prefix = sel.consumed == 0 ? 0u : kmin >> (32 - sel.consumed);
+    if (sel.consumed == 32)
+        return sel;  // all candidates equal: the first k in position order
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t copy = lane % kCopies, dummy = kBins * kCopies + lane;
     constexpr int kPer = kBins / NT;  // bins owned by a thread in the suffix scan
@@ -99,22 +159,25 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
     for (int i = threadIdx.x; i < kBins * kCopies / 4; i += NT)
         reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = digit_shift(pass);
-        const uint32_t dmask = (1u << digit_width(pass)) - 1;
+    for (int pass = 0; pass < 3 && sel.consumed < 32; ++pass) {
+        const int width = min(kDigitBits, 32 - sel.consumed);
+        const int shift = 32 - sel.consumed - width;
+        const uint32_t dmask = (1u << width) - 1;
         // keys whose top `consumed` bits equal the prefix: (x & pmask) == pval (uniform scalars)
         const uint32_t pmask = sel.consumed == 0 ? 0u : ~0u << (32 - sel.consumed);
         const uint32_t pval = sel.consumed == 0 ? 0u : sel.prefix << (32 - sel.consumed);
-        // Pass-0 bin 0 holds key 0 only (a candidate's top 11 bits are never all zero: that would make
-        // it -inf or a NaN): its adds go to the dummy word like those of keys outside the prefix, so
-        // segments padded with zeros do not pile their atomics onto one bin.  (The test is on the
-        // digit, which changes with the pass, not on the key: the compiler would keep 64 loop-invariant
-        // key tests in scalar registers across the passes.)
+        // Key 0 (not a candidate) can match only a zero prefix in pass 0, and then its digit is 0 while
+        // a candidate's is not (a candidate's top 11 bits are never all zero -- that would make it -inf
+        // or a NaN -- and with a zero prefix they all lie in the digit): its add goes to the dummy word
+        // like those of keys outside the prefix, so segments padded with zeros do not pile their
+        // atomics onto one bin.  (The test is on the digit, which changes with the pass, not on the
+        // key: the compiler would keep 64 loop-invariant key tests in scalar registers.)
+        const uint32_t keep0 = (pass != 0 || pval != 0u) ? 1u : 0u;
 #pragma unroll
         for (int m = 0; m < VPT; ++m) {
             const uint32_t x = key[m];
             const uint32_t d = (x >> shift) & dmask;
-            const bool take = (x & pmask) == pval && (d != 0u || pass != 0);
+            const bool take = (x & pmask) == pval && (d | keep0) != 0u;
             atomicAdd(&hist[take ? kCopies * d + copy : dummy], 1u);
         }
         __syncthreads();
@@ -157,8 +220,8 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
         const uint32_t above = *s_above, bin = *s_bin;
         __syncthreads();
         sel.k_rem -= above;
-        sel.prefix = (sel.prefix << digit_width(pass)) | (uint32_t)d;
-        sel.consumed += digit_width(pass);
+        sel.prefix = (sel.prefix << width) | (uint32_t)d;
+        sel.consumed += width;
         if (bin == sel.k_rem) {
             sel.whole = true;
             break;
@@ -254,7 +317,7 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
         return;
     // LDS: the histograms, reused afterwards as the staging area of the picks.
     __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
-    __shared__ uint32_t scratch[2 * NT / kWave];
+    __shared__ uint32_t scratch[3 * NT / kWave];
     __shared__ int s_d;
     __shared__ uint32_t s_above, s_bin;
     const int64_t seg_base = (int64_t)seg * (VPT * NT);
@@ -426,9 +489,14 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
     const uint32_t *fk = in_a ? key_a : key_b;
     const int32_t *fp = in_a ? pos_a : pos_b;
     const int64_t fld = in_a ? lda : ldb;
-    hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0, stream,
-                       nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx, gate.row_mode,
-                       gate.want);
+    if (n_in <= kSegThreads * kFinalVpt)  // (8 segments' picks at 128K columns): half the keys per thread
+        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kFinalVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads),
+                           0, stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,
+                           gate.row_mode, gate.want);
+    else
+        hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0,
+                           stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,
+                           gate.row_mode, gate.want);
     return hipGetLastError();
 }
 

@@ -420,6 +420,9 @@ def main():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--lengths", default="131072,1048576")
     ap.add_argument("--hi-lengths", default="262144,524288,1048576", help="KV lengths of the HI workload")
+    ap.add_argument("--hi-prefill-lengths", default="32768,65536,131072,262144,524288,1048576",
+                    help="KV lengths of the HI chunked-prefill workload")
+    ap.add_argument("--fp8-lengths", default="131072,1048576", help="KV lengths of the FP8 indexer workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="decode", choices=["decode", "hi", "hi_prefill", "fp8", "prefill", "ragged", "tiny", "all"],
                     help="decode prints the metric line; the others print their own figures as one JSON line")
@@ -440,9 +443,11 @@ def main():
             extra["hi_decode_batch8"] = bench_hi(args.steps, args.warmup, lengths=hl)
             extra["hi_decode_batch8_B8"] = bench_hi(args.steps, args.warmup, lengths=hl, B=8)
         if args.workload in ("fp8", "all"):
-            extra["fp8_indexer_decode"] = bench_fp8(args.steps, args.warmup)
+            extra["fp8_indexer_decode"] = bench_fp8(args.steps, args.warmup,
+                                                    lengths=[int(v) for v in args.fp8_lengths.split(",")])
         if args.workload in ("hi_prefill", "all"):
-            extra["hi_prefill_qlen2048_B8"] = bench_hi_prefill(args.steps, args.warmup)
+            extra["hi_prefill_qlen2048_B8"] = bench_hi_prefill(
+                args.steps, args.warmup, lengths=[int(v) for v in args.hi_prefill_lengths.split(",")])
         if args.workload in ("prefill", "all"):
             extra["chunked_prefill_cli"] = bench_prefill(args.steps, args.warmup)
         if args.workload in ("ragged", "all"):

@@ -828,11 +828,16 @@ constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 32 wave-wide 1 K
 constexpr int kMinGroupedRows = 64;                          // fewer rows: the per-row kernel only
 static_assert(kGroupWaves == kGroupRows, "one row per wave");
 
+template <int MODE>
 __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     RowsDev rows, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ keys,
-    int k_sink, int k_swa, float *__restrict__ scores, int64_t ld, int64_t n_cols, int64_t cols_per_block,
-    const uint8_t *row_mode, int want)
+    int k_sink, int k_swa, const int64_t *__restrict__ sb_off, int P, int G, float *__restrict__ scores, int64_t ld,
+    int64_t n_cols, int64_t cols_per_block, const uint8_t *row_mode, int want)
 {
+    // MODE Flat: columns are token positions, keys are k_idx rows.  MODE PageMean (HI stage 1):
+    // columns are sub-blocks, keys their means (k_mean rows from sb_off), and the scores of the G
+    // sub-blocks of a page are summed into one page score.
+    static_assert(MODE == kModeFlat || MODE == kModePageMean, "flat or page-mean columns");
     const int chunk = blockIdx.x, grp = blockIdx.y;
     if (!group_uniform(rows, row_mode, want, grp))
         return;  // the per-row kernel scores these rows
@@ -848,17 +853,30 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     const int g = lane >> 4;
     const int r = grp * kGroupRows + wave;
 
-    // Column ranges (columns are below 2^31): every valid row scores [k_sink, hi_r) with hi_r the
-    // end of its mid region cut at L; lanes 0..15 of every wave take one row each and reduce.
+    // Column ranges (columns are below 2^31): every valid row scores [lo, hi_r) -- flat: from k_sink to
+    // the end of its mid region cut at L; page-mean: the sub-blocks of its causal pages -- and lanes
+    // 0..15 of every wave take one row each and reduce.
     const RowInfo ri0 = row_info(rows, grp * kGroupRows);
-    const int L = (int)ri0.L;
-    const int64_t base = ri0.base;
+    int L = (int)ri0.L;    // keys of the sequence
+    int64_t base = ri0.base;
+    if constexpr (MODE == kModePageMean) {
+        base = sb_off[ri0.seq];
+        L = (int)(sb_off[ri0.seq + 1] - base);
+    }
+    const int n_keys = L;
+    auto last_page = [&](const RowInfo &ri) {  // causal pages p <= floor(t / P) that exist
+        return (int)(min(ri.t, ri.L - 1) / P);
+    };
     auto row_hi = [&](int rr) {
         const RowInfo ri = row_info(rows, rr);
-        const SiRanges gi = si_ranges(ri, k_sink, k_swa);
-        return (int)(gi.mid_hi < ri.L ? gi.mid_hi : ri.L);
+        if constexpr (MODE == kModePageMean) {
+            return ri.valid ? min(n_keys, (last_page(ri) + 1) * G) : 0;
+        } else {
+            const SiRanges gi = si_ranges(ri, k_sink, k_swa);
+            return (int)(gi.mid_hi < ri.L ? gi.mid_hi : ri.L);
+        }
     };
-    const int lo = k_sink;
+    const int lo = MODE == kModePageMean ? 0 : k_sink;
     const int my_hi = row_hi(r);
     int u_hi = row_hi(grp * kGroupRows + n);
     for (int o = 1; o < 16; o <<= 1)
@@ -876,12 +894,14 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     const int cmp_lo = c_begin + st_first * kStageKeys;
     const int cmp_hi = min(c_begin + st_end * kStageKeys, c_end);
 
-    // Columns outside the computed stages hold no score for any row of the group.
+    // Columns outside the computed stages hold no score for any row of the group.  (Page-mean: the
+    // stage and chunk bounds are multiples of G, so these are whole pages.)
     {
         float *o = scores + (int64_t)r * ld;
-        for (int64_t c = c_begin + lane; c < cmp_lo; c += kWave)
+        const int gc = MODE == kModePageMean ? G : 1;
+        for (int64_t c = c_begin / gc + lane; c < cmp_lo / gc; c += kWave)
             o[c] = -INFINITY;
-        for (int64_t c = cmp_hi + lane; c < c_end; c += kWave)
+        for (int64_t c = cmp_hi / gc + lane; c < (c_end + gc - 1) / gc && c < ld; c += kWave)
             o[c] = -INFINITY;
     }
 
@@ -908,6 +928,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
         const int kk0 = 4 * wave + g;
         const int c16 = n ^ (kk0 & 15);
         const uint16_t *kseq = keys + base * kDim;
+        const int my_last_page = MODE == kModePageMean ? last_page(row_info(rows, r)) : 0;
         auto issue_stage = [&](int st, uint16_t *buf) __attribute__((always_inline)) {
             const int col0 = c_begin + st * kStageKeys;
             const uint16_t *ks0 = kseq + (int64_t)col0 * kDim;
@@ -950,6 +971,9 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
         };
 
         // One stage: wait for its DMA, start the next stage's into the other buffer, score 8 tiles.
+        // Page-mean: the G sub-block scores of a page (G consecutive lanes of a lane group; G is a
+        // power of two up to 16) are summed, a sub-block past the sequence adding nothing, and lane
+        // n % G == 0 stores the page score, -inf for pages after the row's last causal page.
         auto run_stage = [&](int st, const uint16_t *buf, uint16_t *next) __attribute__((always_inline)) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA writes have landed
             __syncthreads();                                  // ... and every other wave's
@@ -967,8 +991,17 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
                     v = g == q ? vq : v;
                 }
                 const int rel = (t4 + g) * kTile + n;
-                if (rel < rel_end)
-                    out[col0 + rel] = rel >= rel_lo && rel < rel_hi ? v : -INFINITY;
+                if constexpr (MODE == kModePageMean) {
+                    float pv = col0 + rel < n_keys ? v : 0.0f;
+                    for (int o = 1; o < G; o <<= 1)
+                        pv += __shfl_xor(pv, o, kWave);
+                    const int pg = (col0 + rel) / G;
+                    if (rel < rel_end && (n & (G - 1)) == 0 && pg < ld)
+                        out[pg] = pg <= my_last_page ? pv : -INFINITY;
+                } else {
+                    if (rel < rel_end)
+                        out[col0 + rel] = rel >= rel_lo && rel < rel_hi ? v : -INFINITY;
+                }
             }
         };
         if (st_first & 1)
@@ -1158,12 +1191,14 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
         return hipSuccess;
     if (dtype == 1) {
         const ScoreGeom geo = score_geometry(rows.n_rows, n_cols);
-        const bool grouped = MODE == kModeFlat && rows.n_rows >= kMinGroupedRows;
-        if (grouped) {
-            dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
-            hipLaunchKernelGGL(score_rows_kernel, ggrid, dim3(kGroupThreads), 0, stream, rows, (const uint16_t *)q_idx,
-                               w, (const uint16_t *)keys, k_sink, k_swa, scores, ld, n_cols, geo.chunk_elems,
-                               gate.row_mode, gate.want);
+        const bool grouped = (MODE == kModeFlat || MODE == kModePageMean) && rows.n_rows >= kMinGroupedRows;
+        if constexpr (MODE == kModeFlat || MODE == kModePageMean) {
+            if (grouped) {
+                dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
+                hipLaunchKernelGGL(score_rows_kernel<MODE>, ggrid, dim3(kGroupThreads), 0, stream, rows,
+                                   (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, sb_off, P, P / B,
+                                   scores, ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want);
+            }
         }
         if constexpr (MODE == kModePageMean) {
             dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);

@@ -247,6 +247,33 @@ def test_page_recall_scores_and_pages(B):
     assert np.array_equal(got, want_pages)
 
 
+# Rows for the multi-row page scoring: groups of 16 rows of one sequence (a prefill chunk crossing
+# page edges, one group straddling the end of a partial last page), then rows scored one by one.
+PM_LENGTHS = [20100, 9000]
+PM_ROWS = ([(0, t) for t in range(19940, 20004)]          # 4 uniform groups over the page edge at 19968
+           + [(0, t) for t in range(20084, 20100)]        # a group ending in the partial last page
+           + [(1, 8999), (0, 5000), (1, 4000), (0, 20099), (1, 127), (0, 0), (1, 200)])
+
+
+@pytest.mark.parametrize("B", [8, 128, 32])
+def test_page_scores_grouped_rows(B):
+    x = custom_rows(PM_LENGTHS, PM_ROWS, attn=False, seed=13)
+    o = oracle_inputs(x)
+    P, M = 128, 40
+    sb_off = lsa.sb_offsets(PM_LENGTHS, B)
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], B)
+    km = synth.bits_to_bf16(km_o).to(DEV)
+    ld = (max(PM_LENGTHS) + P - 1) // P + 3
+    ps = torch.empty((len(PM_ROWS), ld), dtype=torch.float32, device=DEV)
+    pages, _ = lsa.lsa_page_recall(rows_of(x), sb_off.to(DEV), x["q_idx"], x["w"], km, P, B, M, page_scores=ps)
+    want_ps = ref.page_scores(o["kv_off"], sb_off.numpy(), o["row_seq"], o["row_pos"], o["q_idx"], o["w"], km_o, P,
+                              B, ld)
+    log("grouped page scores worst err/tol", assert_scores_close(host(ps), want_ps, "page scores"))
+    want_pages = ref.topk(want_ps, M)
+    assert_idx_sets_match(host(pages), want_pages, lambda r, d: near_tie(want_ps[r, d], kth_best(want_ps[r], M)),
+                          what="pages")
+
+
 # --------------------------------------------------------------------------------------------- a8-a10 attention
 
 

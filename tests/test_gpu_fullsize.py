@@ -129,6 +129,49 @@ def test_decode_batch32_full_size(L):
         assert_attn_close(host(out2[r:r + 1]), wo, host(lse2[r:r + 1]), wl, 2e-2, f"attention row {r}")
 
 
+@pytest.mark.parametrize("L", [131072, 1048576])
+def test_fp8_decode_batch32_full_size(L):
+    # The FP8 indexer on the decode batch as bench.py runs it: quantizer codes of sampled keys and of
+    # whole query rows bit for bit, scores at sampled positions, and the selection built on them.
+    from oracle import fp8
+    log(f"FP8 decode batch 32 at L={L}")
+    x = synth.decode_sweep(L, device=DEV)
+    c = x["cfg"]
+    rows = rows_of(x)
+    k8, ks = lsa.lsa_quantize_fp8(x["k_idx"])
+    q8, qs = lsa.lsa_quantize_fp8(x["q_idx"])
+    rng = np.random.default_rng(L + 8)
+    keys = rng.integers(0, 32 * L, 65536)
+    wc, wsc = fp8.quantize(f64(host(x["k_idx"][torch.from_numpy(keys).to(DEV)])))
+    assert np.array_equal(host(k8[torch.from_numpy(keys).to(DEV)]), wc)
+    assert np.array_equal(host(ks[torch.from_numpy(keys).to(DEV)]), wsc)
+    qc, qsc = fp8.quantize(f64(host(x["q_idx"])))
+    assert np.array_equal(host(q8), qc) and np.array_equal(host(qs), qsc)
+    scores = lsa.lsa_index_score_fp8(rows, q8, qs, x["w"], k8, ks, (16, 1024, 1024))
+    for r in (0, 31):
+        k_seq = seq_host(x, r, "k_idx")
+        pos = np.concatenate([rng.integers(0, L, 2048), [0, 15, 16, L - 1026, L - 1025, L - 1024, L - 1]])
+        kc, ksc = fp8.quantize(f64(k_seq[pos]))
+        kd = fp8.dequantize(kc, ksc)
+        qd = fp8.dequantize(qc[r], qsc[r])
+        want = np.array([ref.score_one(qd, host(x["w"][r]), kd[i]) if 16 <= s <= L - 1025 else -np.inf
+                         for i, s in enumerate(pos)], np.float32)
+        assert_scores_close(host(scores[r])[pos][None], want[None], f"FP8 scores row {r}")
+    g_idx = host(lsa.lsa_topk(scores, c["k_sparse"]))
+    check_idx_properties(g_idx, x, c)
+    for b, picks in enumerate(x["needles"]):
+        assert set(picks) <= set(g_idx[b].tolist()), f"needles of sequence {b} not all picked under FP8"
+    if L <= 131072:
+        r = 9
+        o = one_row_oracle(x, r, r)
+        kc, ksc = fp8.quantize(f64(seq_host(x, r, "k_idx")))
+        row_scores = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], fp8.dequantize(qc[r:r + 1], qsc[r:r + 1]),
+                                     o["w"], fp8.dequantize(kc, ksc), 16, 1024, ld=L)
+        w_idx = ref.topk(row_scores, 1024)
+        th = kth_best(row_scores[0], 1024)
+        assert_idx_sets_match(g_idx[r:r + 1], w_idx, lambda _, d: near_tie(row_scores[0][d], th))
+
+
 def check_hi_row_against_oracle(x, r, b, g_idx_row, P=128, B=128, M=1024):
     """The oracle's own HI selection for row r (its own sub-block means, page recall, stage-2 scores,
     top-K) against the GPU's picks; differences only at token- or page-level near-ties."""

@@ -1,8 +1,9 @@
 """FP8 form of the Lightning Indexer's inputs (TEST INFRASTRUCTURE ONLY: the test suite, the smoke
 check and the benchmark's CPU-baseline leg may import it; the HIP library never does).
 
-The pages state only that the indexer supports FP8 computation (LongCat-Flash-Exp paper §2.2,
-"Lightning Indexer"); the format and the scaling are a reading:
+The page "LongCat Sparse Attention: Taming the Lightning via Streaming-aware Hierarchical Cross-Layer
+Indexing" (§2.2, the Lightning Indexer) states only that the indexer supports FP8 computation; the
+format and the scaling are a reading:
 
 * elements: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; subnormals; the
   largest finite magnitude is 448; no infinities; codes 0x7f / 0xff are NaN and never produced);

@@ -388,7 +388,7 @@ def test_attention_bf16_late_dominant_logit(repeat):
 
 
 class OracleRanking:
-    """The oracle's own scores, to judge where GPU and oracle index sets may differ: a position is a
+    """The oracle's own scores, to decide where GPU and oracle index sets may differ: a position is a
     near-tie when its Eq. 1 score is within 1e-3 of the row's K-th best; under HI also when its page
     score is within 1e-3 of the M-th best page score (the page ranking itself tied)."""
 

@@ -67,14 +67,14 @@ def step_distribution(fn, reps, flush_bytes=0):
 
 
 TRAFFIC_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                               "score_stream_kernel_decode_b32_1m_traffic.md")
+                               "index_topk_fused_decode_b32_1m_traffic.md")
 TRAFFIC_L = 1048576
-TRAFFIC_SOURCES = ("index_score.hip", "lsa_dev.hpp", "lsa_kernels.hpp")
+TRAFFIC_SOURCES = ("index_score.hip", "topk.hip", "topk_block.hpp", "lsa_dev.hpp", "lsa_kernels.hpp")
 
 
 def measured_traffic():
-    """HBM bytes per launch of the scoring kernel from the committed rocprofv3 counter summary, or None
-    when the kernel's sources changed since the counters were taken (their hash differs)."""
+    """HBM bytes per lsa_index_topk call (its kernels summed) from the committed rocprofv3 counter summary,
+    or None when the kernels' sources changed since the counters were taken (their hash differs)."""
     import hashlib
     try:
         line = [v for v in open(TRAFFIC_PROFILE).read().splitlines() if v.startswith("traffic:")][0]
@@ -125,9 +125,16 @@ def run_length(L, batch, steps, warmup, seed=0):
     t_step_ev = time_on_stream(step, steps, 0)
     warm = step_distribution(step, steps)
     cold = step_distribution(step, steps, flush_bytes=MALL_FLUSH_BYTES)
-    # The dominant kernel alone: the indexer scoring launch of the layer (same grid, same stream).
-    scores = torch.empty((n, L), dtype=torch.float32, device="cuda")
+    # The dominant kernel: the layer's flat selection (scoring fused with the first top-K level, then the
+    # top-K levels over the candidate lists), as lsa_index_topk launches it for the layer, same stream.
     bud = (c["k_sink"], c["k_swa"], c["k_sparse"])
+    sel = torch.empty((n, c["k_sparse"]), dtype=torch.int32, device="cuda")
+    sel_ws = lsa.lsa_index_topk_workspace(rows, x["q_idx"], c["k_sparse"])
+    t_sel = time_on_stream(lambda: lsa.lsa_index_topk(rows, x["q_idx"], x["w"], x["k_idx"], bud, idx=sel, ws=sel_ws),
+                           steps, warmup)
+    assert torch.equal(sel, idx), "lsa_index_topk and the layer disagree"
+    # For comparison: the scoring kernel alone when it writes the fp32 scores (the unfused pass).
+    scores = torch.empty((n, L), dtype=torch.float32, device="cuda")
     t_score = time_on_stream(lambda: lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], bud, scores=scores),
                              steps, warmup)
     # Needle sanity (not timed): every planted needle is selected.
@@ -140,15 +147,16 @@ def run_length(L, batch, steps, warmup, seed=0):
     io_bytes = n * (64 * 128 * 2 + 64 * 4 + 128 * 576 * 2 + 128 * 512 * 2 + 128 * 4 + c["k_sparse"] * 4)
     alg_bytes = k_bytes + attn_bytes + io_bytes
     flops = n * (mid * 64 * 128 * 2 + (c["k_sink"] + c["k_swa"] + c["k_sparse"]) * 128 * (576 + 512) * 2)
-    del scores
+    del scores, sel, sel_ws
     res = dict(L=L, batch=n, latency_us=t_step * 1e6, latency_us_events=t_step_ev * 1e6,
                warm_us_p10=warm["p10"], warm_us_p50=warm["p50"], warm_us_p90=warm["p90"],
                cold_us_p10=cold["p10"], cold_us_p50=cold["p50"], cold_us_p90=cold["p90"],
-               score_kernel_us=t_score * 1e6, score_kernel_bytes=k_bytes, alg_bytes=alg_bytes, flops=flops,
-               hbm_frac_layer=alg_bytes / t_step / HBM_PEAK, score_kernel_gbs=k_bytes / t_score / 1e9,
-               needle_recall=recall)
-    log(f"[bench] L={L}: layer {t_step * 1e6:.1f} us ({res['hbm_frac_layer'] * 100:.1f}% HBM), score kernel "
-        f"{t_score * 1e6:.1f} us = {res['score_kernel_gbs']:.0f} GB/s, needle recall {recall:.3f}; per call "
+               select_us=t_sel * 1e6, select_gbs=k_bytes / t_sel / 1e9, score_kernel_bytes=k_bytes,
+               unfused_score_kernel_us=t_score * 1e6, unfused_score_kernel_gbs=k_bytes / t_score / 1e9,
+               alg_bytes=alg_bytes, flops=flops, hbm_frac_layer=alg_bytes / t_step / HBM_PEAK, needle_recall=recall)
+    log(f"[bench] L={L}: layer {t_step * 1e6:.1f} us ({res['hbm_frac_layer'] * 100:.1f}% HBM), flat selection "
+        f"{t_sel * 1e6:.1f} us = {res['select_gbs']:.0f} GB/s of keys (unfused scoring alone {t_score * 1e6:.1f} us), "
+        f"needle recall {recall:.3f}; per call "
         f"warm p10/p50/p90 {warm['p10']:.1f}/{warm['p50']:.1f}/{warm['p90']:.1f} us, cold (cache flushed) "
         f"{cold['p10']:.1f}/{cold['p50']:.1f}/{cold['p90']:.1f} us")
     del x, layer, idx, out, lse
@@ -202,7 +210,7 @@ def bench_fp8(steps, warmup, lengths=(131072, 1048576), batch=32):
     return res
 
 
-def cpu_baseline(L=131072, rows=4, batch=32, seed=0):
+def cpu_baseline(L=1048576, rows=2, batch=32, seed=0):
     """The oracle on a bounded sample: `rows` of the 32 rows of the L-token decode batch, one thread
     per row; extrapolated to the whole batch at the same thread count."""
     import numpy as np
@@ -462,7 +470,7 @@ def main():
     lengths = [int(v) for v in args.lengths.split(",")]
     legs = [run_length(L, args.batch, args.steps, args.warmup) for L in lengths]
     head = legs[-1]
-    cpu = None if args.no_cpu_baseline else cpu_baseline(batch=args.batch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(L=head["L"], batch=args.batch)
     line = {
         "metric": "LSA layer fwd latency (us) at 128K/1M decode; % HBM peak and % MFMA peak",
         "value": round(head["latency_us"], 2),
@@ -483,9 +491,10 @@ def main():
         "queries_per_s": round(args.batch / (head["latency_us"] * 1e-6), 1),
         "hbm_frac_layer": round(head["hbm_frac_layer"], 4),
         "mfma_frac_layer": round(head["flops"] / (head["latency_us"] * 1e-6) / BF16_PEAK, 4),
-        "roofline": {"kernel": "score_stream_kernel (flat indexer scoring)", "bound": "hbm",
-                     "achieved": round(head["score_kernel_gbs"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                     "frac": round(head["score_kernel_gbs"] * 1e9 / HBM_PEAK, 4),
+        "roofline": {"kernel": "lsa_index_topk: score_stream_kernel<Flat, 3, select> (indexer scoring fused with "
+                               "the first top-K level) + topk_level_kernel over the candidate lists",
+                     "bound": "hbm", "achieved": round(head["select_gbs"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": round(head["select_gbs"] * 1e9 / HBM_PEAK, 4),
                      "traffic": measured_traffic() if head["L"] == TRAFFIC_L else None,
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "cpu_baseline": cpu,

@@ -78,7 +78,7 @@ typedef struct lsa_budget {
  *   recalled page indices (ascending, -1 = empty slot); column u in [0, M*P) stands for position
  *   pages[r, u/P]*P + u%P and gets its score when that position is in mid(t) and < L_b, else -inf;
  *   columns [M*P, ld_scores) get -inf.  Requires ld_scores >= M*P, P % 16 == 0.
- * Supported: fp32 with n_heads <= 64, head_dim <= 128 (head_dim % 4 == 0); bf16 with
+ * Supported: fp32 with 1 <= n_heads <= 64 and head_dim 64 or 128; bf16 with
  *   (n_heads, head_dim) = (64, 128) on matrix cores.
  */
 int lsa_index_score(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
@@ -166,6 +166,24 @@ int lsa_page_recall_workspace_size(const lsa_rows_t *rows, int32_t P, int32_t M,
 int lsa_topk(int32_t n_rows, const float *scores, int64_t ld_scores, int64_t n_cols, const int32_t *pages,
              int32_t M, int32_t P, int32_t k, int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
 int lsa_topk_workspace_size(int32_t n_rows, int64_t n_cols, int32_t k, size_t *bytes);
+
+/*
+ * The flat token selection in one call ([paper] §2.2 Eq. 1-2 over the SI middle region, [paper]
+ * §3.1): idx [n_rows, budget.k_sparse] receives exactly what lsa_topk(k = budget.k_sparse) returns
+ * for the flat scores of lsa_index_score (pages == NULL) -- the positions of the k_sparse best
+ * mid(t) tokens under (score desc, position asc), ascending, -1 padded -- bit for bit.  When the
+ * rows are scored one by one on matrix cores (bf16, 64 heads x 128 dims, fewer than 64 rows, enough
+ * 8192-column chunks to fill the chip) scoring and the first top-K level run in one pass: each
+ * block keeps its chunk's scores on chip and writes only its k best (score, position) pairs, so
+ * the scores never reach HBM.  Otherwise the scores go through the workspace and lsa_topk.
+ * Arguments, shapes, supported dtypes and errors are those of lsa_index_score and lsa_topk;
+ * 1 <= k_sparse <= 4096.  Workspace: lsa_index_topk_workspace_size() bytes, 256-byte aligned.
+ */
+int lsa_index_topk(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                   int32_t n_heads, int32_t head_dim, lsa_budget_t budget, int32_t *idx, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+int lsa_index_topk_workspace_size(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim,
+                                  int32_t k_sparse, size_t *bytes);
 
 /*
  * Hybrid sparse attention over the MLA latent ([paper] §4.1.1 HFA; attention of [summary] "DSA

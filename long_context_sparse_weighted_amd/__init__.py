@@ -18,7 +18,7 @@ LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = r
 LSA_F32, LSA_BF16 = 0, 1
 
 SYMBOLS = ("lsa_index_score", "lsa_quantize_fp8", "lsa_index_score_fp8", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
-           "lsa_topk_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
+           "lsa_topk_workspace_size", "lsa_index_topk", "lsa_index_topk_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
            "lsa_layer_workspace_size", "lsa_status_string", "lsa_last_error")
 
 
@@ -66,6 +66,8 @@ def lib():
         L.lsa_page_recall_workspace_size.argtypes = [RP, I32, I32, ctypes.POINTER(SZ)]
         L.lsa_topk.argtypes = [I32, P, I64, I64, P, I32, I32, I32, P, P, SZ, P]
         L.lsa_topk_workspace_size.argtypes = [I32, I64, I32, ctypes.POINTER(SZ)]
+        L.lsa_index_topk.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, P, SZ, P]
+        L.lsa_index_topk_workspace_size.argtypes = [ctypes.c_int, RP, I32, I32, I32, ctypes.POINTER(SZ)]
         L.lsa_hybrid_attn.argtypes = [ctypes.c_int, RP, P, P, I32, I32, I32, F, Budget, P, P, P, P, P, SZ, P]
         L.lsa_hybrid_attn_workspace_size.argtypes = [ctypes.c_int, RP, I32, I32, Budget, ctypes.POINTER(SZ)]
         L.lsa_layer_fwd.argtypes = [ctypes.POINTER(LayerCfg), RP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -244,6 +246,32 @@ def lsa_topk(scores, k, n_cols=None, pages=None, P=0, idx=None):
     M = 0 if pages is None else pages.shape[1]
     _check(lib().lsa_topk(n_rows, _p(scores), ld, int(n_cols), _p(pages), M, int(P), int(k), _p(idx), wp, wn,
                           _stream()))
+    return idx
+
+
+def lsa_index_topk_workspace(rows: RowsDesc, q_idx, k_sparse):
+    """A workspace tensor for lsa_index_topk on these rows (reusable across calls of the same shape)."""
+    n_rows, HI, dI = q_idx.shape
+    sz = ctypes.c_size_t()
+    _check(lib().lsa_index_topk_workspace_size(_dt(q_idx), ctypes.byref(rows.c()), HI, dI, int(k_sparse),
+                                               ctypes.byref(sz)))
+    return _workspace(sz.value, q_idx.device)
+
+
+def lsa_index_topk(rows: RowsDesc, q_idx, w, k_idx, budget, idx=None, ws=None):
+    """idx [n_rows, k_sparse] int32: the flat token selection (indexer scores and top-K in one call)."""
+    n_rows, HI, dI = q_idx.shape
+    dt = _dt(q_idx)
+    _need(k_idx, q_idx.dtype, "k_idx")
+    _need(w, torch.float32, "w")
+    bud = Budget(*budget)
+    if ws is None:
+        ws = lsa_index_topk_workspace(rows, q_idx, bud.k_sparse)
+    wp, wn = _aligned(ws)
+    if idx is None:
+        idx = torch.empty((n_rows, bud.k_sparse), dtype=torch.int32, device=q_idx.device)
+    _check(lib().lsa_index_topk(dt, ctypes.byref(rows.c()), _p(q_idx), _p(w), _p(k_idx), HI, dI, bud, _p(idx), wp,
+                                wn, _stream()))
     return idx
 
 

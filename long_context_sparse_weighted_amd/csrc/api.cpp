@@ -115,7 +115,6 @@ int check_page_geometry(int dtype, int32_t P, int32_t B, int32_t M)
 // Workspace layout of lsa_layer_fwd.
 struct LayerWs {
     uint8_t *row_mode;
-    float *flat_scores;
     void *topk_ws;
     float *page_scores;
     int32_t *pages;
@@ -125,6 +124,61 @@ struct LayerWs {
     size_t bytes;
 };
 
+// The fused flat pass works on fixed chunks of columns per block: it needs rows that are scored one by
+// one, and enough chunks to give every CU at least one block (a 32-row batch from 64K columns on;
+// below that the separate passes, whose chunks shrink with the work, are faster).
+bool flat_fused(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k)
+{
+    return index_select_fusable(dtype, rows->n_rows, n_heads, head_dim, k) &&
+           (int64_t)rows->n_rows * index_select_fused_segments(rows->max_kv_len) >= 256;
+}
+bool flat_fused(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows)
+{
+    return flat_fused(cfg->dtype, rows, cfg->n_heads_idx, cfg->head_dim_idx, cfg->budget.k_sparse);
+}
+
+// Workspace of the flat selection (lsa_index_topk and the layer's flat rows): candidate lists of the
+// fused pass, or the scores and the top-K lists of the separate passes; the scores come first.
+size_t flat_select_bytes(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k, size_t *scores_bytes)
+{
+    const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
+    if (flat_fused(dtype, rows, n_heads, head_dim, k)) {
+        *scores_bytes = 0;
+        return topk_lists_workspace_bytes(rows->n_rows, index_select_fused_segments(ld), k);
+    }
+    *scores_bytes = align_up(sizeof(float) * (size_t)rows->n_rows * (size_t)ld);
+    return *scores_bytes + topk_workspace_bytes(rows->n_rows, ld, k);
+}
+
+hipError_t launch_flat_select(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                              int n_heads, int head_dim, lsa_budget_t bud, int32_t *idx, void *ws, RowGate gate,
+                              hipStream_t stream)
+{
+    const RowsDev rd = to_dev(rows);
+    const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
+    if (flat_fused(dtype, rows, n_heads, head_dim, bud.k_sparse)) {
+        // scoring and the first top-K level in one pass; the scores never leave the chip
+        const int64_t n_seg = index_select_fused_segments(ld);
+        uint32_t *sk;
+        int32_t *sp;
+        int64_t sld;
+        topk_first_lists(ws, rows->n_rows, n_seg, bud.k_sparse, &sk, &sp, &sld);
+        hipError_t e = launch_index_select_fused(rd, q_idx, w, k_idx, bud.k_sink, bud.k_swa, ld, bud.k_sparse, sk, sp,
+                                                 sld, gate, stream);
+        if (e != hipSuccess)
+            return e;
+        return launch_topk_lists(rows->n_rows, n_seg, bud.k_sparse, ws, idx, gate, stream);
+    }
+    size_t sb;
+    (void)flat_select_bytes(dtype, rows, n_heads, head_dim, bud.k_sparse, &sb);
+    float *scores = (float *)ws;
+    hipError_t e = launch_index_score(dtype, rd, rows->max_kv_len, q_idx, w, k_idx, n_heads, head_dim, bud.k_sink,
+                                      bud.k_swa, nullptr, 0, 1, scores, ld, gate, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_topk(rows->n_rows, scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, (char *)ws + sb, gate, stream);
+}
+
 LayerWs layer_ws_layout(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, bool use_hi, void *base)
 {
     Carver c(base);
@@ -133,9 +187,10 @@ LayerWs layer_ws_layout(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, bool
     const int k_total = cfg->budget.k_sink + cfg->budget.k_swa + cfg->budget.k_sparse;
     if (cfg->is_owner) {
         w.row_mode = (uint8_t *)c.take((size_t)n);
-        w.flat_scores = (float *)c.take(sizeof(float) * (size_t)n * (size_t)rows->max_kv_len);
-        // The flat and the HI token top-K share one workspace.
-        size_t tk = topk_workspace_bytes((int)n, rows->max_kv_len > 0 ? rows->max_kv_len : 1, cfg->budget.k_sparse);
+        // The flat and the HI token top-K share one workspace.  Rows scored one by one take the fused
+        // scoring + first top-K level, which writes candidate lists instead of scores.
+        size_t sb;
+        size_t tk = flat_select_bytes(cfg->dtype, rows, cfg->n_heads_idx, cfg->head_dim_idx, cfg->budget.k_sparse, &sb);
         if (use_hi) {
             const size_t hk = topk_workspace_bytes((int)n, (int64_t)cfg->M * cfg->P, cfg->budget.k_sparse);
             tk = hk > tk ? hk : tk;
@@ -426,6 +481,55 @@ int lsa_topk(int32_t n_rows, const float *scores, int64_t ld_scores, int64_t n_c
     return hip_status(e, "lsa_topk launch");
 }
 
+static int check_index_topk(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k)
+{
+    if (dtype != LSA_F32 && dtype != LSA_BF16)
+        return fail(LSA_ERR_INVALID, "dtype must be LSA_F32 or LSA_BF16");
+    if (int st = check_rows(rows))
+        return st;
+    if (!index_score_supported(dtype, n_heads, head_dim))
+        return fail(LSA_ERR_UNSUPPORTED, "indexer shape (%d heads, dim %d) not compiled for this dtype", n_heads,
+                    head_dim);
+    if (k < 1 || k > 4096)
+        return fail(LSA_ERR_UNSUPPORTED, "k_sparse must be in [1, 4096]");
+    return LSA_OK;
+}
+
+int lsa_index_topk_workspace_size(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim,
+                                  int32_t k_sparse, size_t *bytes)
+{
+    if (!bytes)
+        return fail(LSA_ERR_INVALID, "bytes is NULL");
+    if (int st = check_index_topk(dtype, rows, n_heads, head_dim, k_sparse))
+        return st;
+    size_t sb;
+    *bytes = flat_select_bytes(dtype, rows, n_heads, head_dim, k_sparse, &sb);
+    return ok();
+}
+
+int lsa_index_topk(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                   int32_t n_heads, int32_t head_dim, lsa_budget_t budget, int32_t *idx, void *ws, size_t ws_bytes,
+                   hipStream_t stream)
+{
+    if (int st = check_index_topk(dtype, rows, n_heads, head_dim, budget.k_sparse))
+        return st;
+    if (int st = check_budget(budget))
+        return st;
+    if (rows->n_rows > 0 && (!q_idx || !w || !k_idx || !idx))
+        return fail(LSA_ERR_INVALID, "q_idx, w, k_idx and idx must be device pointers");
+    size_t sb;
+    const size_t need = flat_select_bytes(dtype, rows, n_heads, head_dim, budget.k_sparse, &sb);
+    if (ws_bytes < need || (need && !ws))
+        return fail(LSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+    if (ws && !aligned256(ws))
+        return fail(LSA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (rows->n_rows == 0)
+        return ok();
+    hipError_t e = launch_flat_select(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, budget, idx, ws,
+                                      RowGate{nullptr, 0}, stream);
+    return hip_status(e, "lsa_index_topk launch");
+}
+
 int lsa_hybrid_attn_workspace_size(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t d_v,
                                    lsa_budget_t budget, size_t *bytes)
 {
@@ -530,15 +634,10 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
         if (need_modes)
             e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
         const uint8_t *gate = need_modes ? lw.row_mode : nullptr;
-        const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
         // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
         if (e == hipSuccess && !all_hi)
-            e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
-                                   cfg->head_dim_idx, bud.k_sink, bud.k_swa, nullptr, 0, 1, lw.flat_scores, ld,
-                                   RowGate{gate, 1}, stream);
-        if (e == hipSuccess && !all_hi)
-            e = launch_topk(rows->n_rows, lw.flat_scores, ld, ld, nullptr, 0, 1, bud.k_sparse, idx, lw.topk_ws,
-                            RowGate{gate, 1}, stream);
+            e = launch_flat_select(cfg->dtype, rows, q_idx, w, k_idx, cfg->n_heads_idx, cfg->head_dim_idx, bud, idx,
+                                   lw.topk_ws, RowGate{gate, 1}, stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);

@@ -18,6 +18,7 @@
 //
 // fp32 path: one thread per key with the key row in VGPRs and q / w in LDS (small configs).
 #include "lsa_kernels.hpp"
+#include "topk_block.hpp"
 
 #include <type_traits>
 #include <utility>
@@ -331,6 +332,11 @@ __device__ inline void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Fused scoring + first top-K level (decode): columns per block, ring depth (3 x 16 KB per block, then
+// reused by the selection) and 32 KB of staged scores: 80 KB, two blocks per CU.
+constexpr int kFusedCols = 8192;
+constexpr int kFusedRing = 3;
+
 // Block -> (row, chunk) of the streaming kernels.  Blocks go to the 8 XCDs in turn, in launch order
 // (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  A paged row's chunks can
 // differ a lot in work (a recall list that is mostly padding leaves its last chunks empty), so paged
@@ -387,16 +393,23 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
     }
 }
 
-template <int MODE, int S>
+// SELECT (flat decode rows): instead of writing its scores, the block keeps them in LDS and writes its
+// chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
+// (sel_key / sel_pos [row][chunk * k_sel ..], key 0 / position -1 padded), so the fp32 scores never go
+// to HBM (their write traffic, interleaved with the key stream, slowed the stream by ~15 % at 1M).
+template <int MODE, int S, bool SELECT>
 __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ keys, int k_sink, int k_swa,
                                                             const int32_t *__restrict__ pages, int M, int P,
                                                             float *__restrict__ scores, int64_t ld, int64_t n_cols,
                                                             int64_t cols_per_block, const uint8_t *row_mode, int want,
-                                                            int grouped)
+                                                            int grouped, int k_sel, uint32_t *__restrict__ sel_key,
+                                                            int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * (kLdsWords + 16)),
+                  "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
     stream_block<MODE>(r, chunk);
@@ -405,6 +418,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
         return;  // scored by the multi-row kernel
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
+    __shared__ __attribute__((aligned(16))) float sbuf[SELECT ? kFusedCols : 1];  // SELECT: the chunk's scores
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -419,166 +433,205 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     // Columns of this chunk that can hold keys: [c_begin, c_end); the others are written -inf.
     int64_t c_begin, c_end;
     chunk_key_range<MODE>(cm, c_first, c_last, c_begin, c_end);
-    if (cm.lo >= cm.hi || c_begin >= c_end) {  // no keys here (the DMAs below need a row of keys)
-        for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
+    const bool empty = cm.lo >= cm.hi || c_begin >= c_end;  // no keys here (the DMAs need a row of keys)
+    if constexpr (!SELECT) {
+        if (empty) {
+            for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
+                out[c] = -INFINITY;
+            return;
+        }
+        for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
             out[c] = -INFINITY;
-        return;
+        for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
+            out[c] = -INFINITY;
     }
-    for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
-        out[c] = -INFINITY;
-    for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
-        out[c] = -INFINITY;
-    u32x4 qa[4][4];
-    const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qa[mt][ks] = src[4 * ks];
-    }
-    float wv[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wv[mt][i] = v[i];
-    }
-
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            loaded_here(qa[mt][ks]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            loaded_here(wv[mt][i]);
-    }
-
-    // This wave's tiles: groups of 4 consecutive tiles (64 columns) go to the waves in turn, so the
-    // block reads one dense window; step k of this wave is tile k % 4 of its group k / 4.  Steps
-    // past the wave's K use its last step's tile again (a tile past the chunk, in the last group,
-    // re-reads the chunk's last tile).
-    constexpr int W = kWavesPerBlock;
-    const int64_t chunk_tile = c_begin / kTile;
-    const int64_t end_tile = (c_end + kTile - 1) / kTile;
-    const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
-    const int64_t K = wave < n_groups ? 4 * ((n_groups - wave + W - 1) / W) : 0;
-    auto tile_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
-        return chunk_tile + 4 * ((k >> 2) * W + wave) + (k & 3);
-    };
-    const int64_t safe_key = cm.base + cm.lo;
-    const uint32_t ring_base =
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&ring[0][wave][0];
-    constexpr uint32_t kSlotBytes = kWavesPerBlock * kTile * kDim * 2;
-    // Token position of the first column of a tile (-1: the tile holds no token).  A tile lies in
-    // one page (P is a multiple of 16), so the page table is read once per tile, by a scalar load.
-    auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
-        const int64_t c0 = tile * kTile;
-        if constexpr (MODE == kModeFlat) {
-            return c0;
-        } else {
-            // (columns and slots fit in 32 bits; readfirstlane keeps the index in scalar registers)
-            const int slot = __builtin_amdgcn_readfirstlane((int)page_slot(cm, (uint32_t)c0));
-            if (slot >= cm.M)
-                return -1;
-            const int64_t pg = pages[(int64_t)r * M + slot];
-            return pg < 0 ? -1 : pg * cm.P + (c0 - (int64_t)slot * cm.P);
-        }
-    };
-    auto key_of = [&](int64_t tp, int i) __attribute__((always_inline)) -> int64_t {
-        const int64_t sp = tp + i;
-        return (tp >= 0 && sp >= cm.lo && sp < cm.hi) ? cm.base + sp : -1;
-    };
-    // A tile is interior when all 16 of its columns hold keys (every tile but those at the ends of
-    // the scored range); the DMA, the scoring and the store then need no per-lane checks.
-    auto interior = [&](int64_t tp) __attribute__((always_inline)) {
-        return tp >= cm.lo && tp + kTile <= cm.hi;
-    };
-    // DMA instruction j of a tile fills bytes 1024 j .. 1024 j + 1023 of its buffer: key 4 j + g,
-    // chunk n ^ (4 j + g); lane_off[j] is that key and chunk's byte offset from the tile's first key.
-    uint32_t lane_off[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        lane_off[j] = (uint32_t)((4 * j + g) * kDim * 2 + (n ^ (4 * j + g)) * 16);
-    auto issue = [&](int64_t k) __attribute__((always_inline)) {
-        const int64_t tile = min(tile_of(k < K ? k : K - 1), end_tile - 1);
-        const int64_t tp = tile_pos(tile);
-        const uint32_t buf = ring_base + (uint32_t)(k % S) * kSlotBytes;
-        if (interior(tp)) {
-            const uint16_t *kb = keys + (cm.base + tp) * kDim;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                dma_16s(kb, lane_off[j], buf + j * 1024);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kk = 4 * j + g;
-                const int64_t key = key_of(tp, kk);
-                const int64_t row_k = key >= 0 ? key : safe_key;
-                dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
-            }
-        }
-    };
-    // Score of tile k (token position tp of its first column) for key n; every lane group ends with
-    // the same 16 values.
-    // The tile's operands move from its ring slot to registers first; once those LDS reads are done
-    // the slot takes the DMA of tile k + S, so all S slots are in flight during the arithmetic.
-    auto score_tile = [&](int64_t k, int64_t tp) __attribute__((always_inline)) -> float {
-        wait_vmcnt<4 * (S - 1)>();  // DMA(k) has landed: only DMA(k + 1 .. k + S - 1) may follow it
-        const bool any = interior(tp) || __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
-        u32x4 b[4];
-        if (any) {
-            const uint16_t *krow = &ring[k % S][wave][n * kDim];
-#pragma unroll
+    if (!empty) {  // (SELECT: a block without keys still publishes its empty candidate list below)
+        u32x4 qa[4][4];
+        const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
+    #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
+    #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+                qa[mt][ks] = src[4 * ks];
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot k % S is free again
-        issue(k + S);
-        float v = 0.0f;
-        if (any) {
-            f32x4 acc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
-                                                                      acc[mt], 0, 0, 0);
+        float wv[4][4];
+    #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
+    #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wv[mt][i] = v[i];
+        }
+
+    #pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+    #pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                loaded_here(qa[mt][ks]);
+    #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                loaded_here(wv[mt][i]);
+        }
+
+        // This wave's tiles: groups of 4 consecutive tiles (64 columns) go to the waves in turn, so the
+        // block reads one dense window; step k of this wave is tile k % 4 of its group k / 4.  Steps
+        // past the wave's K use its last step's tile again (a tile past the chunk, in the last group,
+        // re-reads the chunk's last tile).
+        constexpr int W = kWavesPerBlock;
+        const int64_t chunk_tile = c_begin / kTile;
+        const int64_t end_tile = (c_end + kTile - 1) / kTile;
+        const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
+        const int64_t K = wave < n_groups ? 4 * ((n_groups - wave + W - 1) / W) : 0;
+        auto tile_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
+            return chunk_tile + 4 * ((k >> 2) * W + wave) + (k & 3);
+        };
+        const int64_t safe_key = cm.base + cm.lo;
+        const uint32_t ring_base =
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&ring[0][wave][0];
+        constexpr uint32_t kSlotBytes = kWavesPerBlock * kTile * kDim * 2;
+        // Token position of the first column of a tile (-1: the tile holds no token).  A tile lies in
+        // one page (P is a multiple of 16), so the page table is read once per tile, by a scalar load.
+        auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
+            const int64_t c0 = tile * kTile;
+            if constexpr (MODE == kModeFlat) {
+                return c0;
+            } else {
+                // (columns and slots fit in 32 bits; readfirstlane keeps the index in scalar registers)
+                const int slot = __builtin_amdgcn_readfirstlane((int)page_slot(cm, (uint32_t)c0));
+                if (slot >= cm.M)
+                    return -1;
+                const int64_t pg = pages[(int64_t)r * M + slot];
+                return pg < 0 ? -1 : pg * cm.P + (c0 - (int64_t)slot * cm.P);
             }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v += wv[mt][i] * relu(acc[mt][i]);
-            v = sum_xor32(sum_xor16(v));
+        };
+        auto key_of = [&](int64_t tp, int i) __attribute__((always_inline)) -> int64_t {
+            const int64_t sp = tp + i;
+            return (tp >= 0 && sp >= cm.lo && sp < cm.hi) ? cm.base + sp : -1;
+        };
+        // A tile is interior when all 16 of its columns hold keys (every tile but those at the ends of
+        // the scored range); the DMA, the scoring and the store then need no per-lane checks.
+        auto interior = [&](int64_t tp) __attribute__((always_inline)) {
+            return tp >= cm.lo && tp + kTile <= cm.hi;
+        };
+        // DMA instruction j of a tile fills bytes 1024 j .. 1024 j + 1023 of its buffer: key 4 j + g,
+        // chunk n ^ (4 j + g); lane_off[j] is that key and chunk's byte offset from the tile's first key.
+        uint32_t lane_off[4];
+    #pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lane_off[j] = (uint32_t)((4 * j + g) * kDim * 2 + (n ^ (4 * j + g)) * 16);
+        auto issue = [&](int64_t k) __attribute__((always_inline)) {
+            const int64_t tile = min(tile_of(k < K ? k : K - 1), end_tile - 1);
+            const int64_t tp = tile_pos(tile);
+            const uint32_t buf = ring_base + (uint32_t)(k % S) * kSlotBytes;
+            if (interior(tp)) {
+                const uint16_t *kb = keys + (cm.base + tp) * kDim;
+    #pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    dma_16s(kb, lane_off[j], buf + j * 1024);
+            } else {
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kk = 4 * j + g;
+                    const int64_t key = key_of(tp, kk);
+                    const int64_t row_k = key >= 0 ? key : safe_key;
+                    dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
+                }
+            }
+        };
+        // Score of tile k (token position tp of its first column) for key n; every lane group ends with
+        // the same 16 values.
+        // The tile's operands move from its ring slot to registers first; once those LDS reads are done
+        // the slot takes the DMA of tile k + S, so all S slots are in flight during the arithmetic.
+        auto score_tile = [&](int64_t k, int64_t tp) __attribute__((always_inline)) -> float {
+            wait_vmcnt<4 * (S - 1)>();  // DMA(k) has landed: only DMA(k + 1 .. k + S - 1) may follow it
+            const bool any = interior(tp) || __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
+            u32x4 b[4];
+            if (any) {
+                const uint16_t *krow = &ring[k % S][wave][n * kDim];
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot k % S is free again
+            issue(k + S);
+            float v = 0.0f;
+            if (any) {
+                f32x4 acc[4];
+    #pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+                    acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+    #pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
+                                                                          acc[mt], 0, 0, 0);
+                }
+    #pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        v += wv[mt][i] * relu(acc[mt][i]);
+                v = sum_xor32(sum_xor16(v));
+            }
+            return v;
+        };
+        if (K > 0) {
+            for (int k = 0; k < S; ++k)
+                issue(k);
+            // Groups of 4 tiles: lane group g stores tile g's 16 scores, so one store instruction writes
+            // 256 contiguous bytes (whole lines).  The DMA waits above count DMA instructions only: a
+            // store between the DMA of a tile and its wait only makes the wait stricter.
+            for (int64_t k0 = 0; k0 < K; k0 += 4) {
+                const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
+                const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
+                const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
+                const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
+                const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+                const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
+                const int64_t c = tile_of(k0 + g) * kTile + n;
+                const bool valid = key_of(tp, n) >= 0;
+                if (c < c_end) {
+                    if constexpr (SELECT)
+                        sbuf[c - c_first] = valid ? v : -INFINITY;
+                    else
+                        out[c] = valid ? v : -INFINITY;
+                }
+            }
+            wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
         }
-        return v;
-    };
-    if (K > 0) {
-        for (int k = 0; k < S; ++k)
-            issue(k);
-        // Groups of 4 tiles: lane group g stores tile g's 16 scores, so one store instruction writes
-        // 256 contiguous bytes (whole lines).  The DMA waits above count DMA instructions only: a
-        // store between the DMA of a tile and its wait only makes the wait stricter.
-        for (int64_t k0 = 0; k0 < K; k0 += 4) {
-            const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
-            const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
-            const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
-            const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
-            const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
-            const int64_t c = tile_of(k0 + g) * kTile + n;
-            const bool valid = key_of(tp, n) >= 0;
-            if (c < c_end)
-                out[c] = valid ? v : -INFINITY;
+    }
+    if constexpr (SELECT) {
+        __syncthreads();  // every wave's scores are in sbuf, every wave's ring DMA has landed
+        // Keys of the chunk: thread t takes columns c_first + 32 t .. + 31 (position order).
+        constexpr int kV = kFusedCols / 256;
+        uint32_t key[kV];
+#pragma unroll
+        for (int m = 0; m < kV; ++m) {
+            const int64_t c = c_first + kV * (int64_t)threadIdx.x + m;
+            const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[c - c_first] : -INFINITY;
+            key[m] = is_candidate(v) ? float_order_key(v) : 0u;
         }
-        wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
+        // The ring is free now: histograms, then the picks, and the selection's scalars after them.
+        uint32_t *lds = reinterpret_cast<uint32_t *>(&ring[0][0][0]);
+        uint32_t *scratch = lds + kLdsWords;
+        int *s_d = reinterpret_cast<int *>(scratch + 12);
+        uint32_t *s_above = scratch + 13, *s_bin = scratch + 14;
+        const Selection sel = block_select<256, kV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
+        uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
+        __syncthreads();
+        const uint32_t n_sel = block_emit<256, kV>(key, sel, scratch, stage_key, stage_li,
+                                                   (uint32_t)(kV * threadIdx.x));
+        __syncthreads();
+        uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
+        int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
+        for (int i = threadIdx.x; i < k_sel; i += blockDim.x) {
+            const bool ok = (uint32_t)i < n_sel;
+            kout[i] = ok ? stage_key[i] : 0u;
+            pout[i] = ok ? (int32_t)(c_first + stage_li[i]) : -1;
+        }
     }
 }
 
@@ -1208,9 +1261,10 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
         } else {
             const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
-            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing>), grid, dim3(256), 0, stream, rows,
+            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, false>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
-                               ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
+                               ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
+                               nullptr, 0);
         }
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
@@ -1280,6 +1334,28 @@ hipError_t launch_quantize_fp8(int dtype, int64_t n_vec, int dim, const void *x,
     else
         hipLaunchKernelGGL(quantize_fp8_kernel<float>, grid, dim3(256), 0, stream, (const float *)x, n_vec, dim, codes,
                            scale);
+    return hipGetLastError();
+}
+
+bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int k)
+{
+    return dtype == 1 && n_heads == kHeads && head_dim == kDim && n_rows < kMinGroupedRows && k >= 1 &&
+           k <= kMaxLocalK;
+}
+
+int64_t index_select_fused_segments(int64_t n_cols) { return (n_cols + kFusedCols - 1) / kFusedCols; }
+
+hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
+                                     int k_sink, int k_swa, int64_t n_cols, int k, uint32_t *sel_key,
+                                     int32_t *sel_pos, int64_t sel_ld, RowGate gate, hipStream_t stream)
+{
+    if (rows.n_rows == 0 || n_cols == 0)
+        return hipSuccess;
+    dim3 grid((unsigned)index_select_fused_segments(n_cols), (unsigned)rows.n_rows);
+    hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, true>), grid, dim3(256), 0, stream, rows,
+                       (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
+                       (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
+                       sel_ld);
     return hipGetLastError();
 }
 

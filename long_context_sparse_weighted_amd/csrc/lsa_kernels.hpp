@@ -16,6 +16,11 @@ struct RowGate {
 };
 
 // --- top-k (topk.hip): exact selection of the k best (score desc, position asc), 1 <= k <= 4096.
+// First-level candidate lists computed elsewhere (n_seg lists of k per row): their workspace, the
+// buffers to fill, and the remaining levels down to idx.
+size_t topk_lists_workspace_bytes(int n_rows, int64_t n_seg, int k);
+void topk_first_lists(void *ws, int n_rows, int64_t n_seg, int k, uint32_t **key, int32_t **pos, int64_t *ld);
+hipError_t launch_topk_lists(int n_rows, int64_t n_seg, int k, void *ws, int32_t *idx, RowGate gate, hipStream_t stream);
 size_t topk_workspace_bytes(int n_rows, int64_t n_cols, int k);
 hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages, int M,
                        int P, int k, int32_t *idx, void *ws, RowGate gate, hipStream_t stream);
@@ -33,6 +38,14 @@ bool index_score_supported(int dtype, int n_heads, int head_dim);
 hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len, const int64_t *sb_off,
                               const void *q_idx, const float *w, const void *k_mean, int n_heads, int head_dim,
                               int P, int B, float *page_scores, int64_t ld_ps, RowGate gate, hipStream_t stream);
+
+// --- fused flat scoring + first top-K level (index_score.hip), for rows scored one by one (fewer than
+// 64 rows: no 16-row groups); segments of index_select_fused_cols() columns
+bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int k);
+int64_t index_select_fused_segments(int64_t n_cols);
+hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
+                                     int k_sink, int k_swa, int64_t n_cols, int k, uint32_t *sel_key,
+                                     int32_t *sel_pos, int64_t sel_ld, RowGate gate, hipStream_t stream);
 
 // --- FP8 indexer (index_score.hip): E4M3 codes, one power-of-two scale per vector
 hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,

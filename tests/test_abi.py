@@ -136,6 +136,36 @@ def test_fp8_validation(L):
                                    None) == L.LSA_ERR_INVALID
 
 
+def test_index_topk_validation_and_workspace(L):
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    b = L.Budget(16, 1024, 1024)
+    sz = ctypes.c_size_t()
+    ws_size = lambda dt, r, H=64, D=128, k=1024: lib.lsa_index_topk_workspace_size(dt, ctypes.byref(r), H, D, k,
+                                                                                   ctypes.byref(sz))
+    # a 32-row bf16 decode batch at 1M tokens takes the fused pass: candidate lists, no score matrix
+    big = _rows(L, 32, 32, 1 << 20)
+    assert ws_size(1, big) == L.LSA_OK
+    assert 0 < sz.value < 32 * (1 << 20) * 4 // 3      # (score, position) lists of 1024 per 8192 columns
+    # fp32, or rows too few to fill the chip: the scores go through the workspace
+    assert ws_size(0, _rows(L, 32, 32, 1 << 20), 4, 64) == L.LSA_OK and sz.value >= 32 * (1 << 20) * 4
+    assert ws_size(1, _rows(L, 1, 1, 20000)) == L.LSA_OK and sz.value >= 20000 * 4
+    assert ws_size(1, big, 32) == L.LSA_ERR_UNSUPPORTED
+    assert ws_size(1, big, k=0) == L.LSA_ERR_UNSUPPORTED
+    assert ws_size(1, big, k=4097) == L.LSA_ERR_UNSUPPORTED
+    assert ws_size(5, big) == L.LSA_ERR_INVALID
+    assert lib.lsa_index_topk_workspace_size(1, ctypes.byref(big), 64, 128, 1024, None) == L.LSA_ERR_INVALID
+    call = lambda r, ws, n, bud=b, idx=fake: lib.lsa_index_topk(1, ctypes.byref(r), fake, fake, fake, 64, 128, bud,
+                                                                idx, ws, n, None)
+    assert ws_size(1, big) == L.LSA_OK
+    assert call(big, fake, sz.value - 1) == L.LSA_ERR_WORKSPACE
+    assert call(big, None, sz.value) == L.LSA_ERR_WORKSPACE
+    assert call(big, ctypes.c_void_p(0x1010), sz.value) == L.LSA_ERR_INVALID      # not 256-byte aligned
+    assert call(big, fake, sz.value, idx=None) == L.LSA_ERR_INVALID
+    assert call(big, fake, sz.value, bud=L.Budget(-1, 1024, 1024)) == L.LSA_ERR_INVALID
+    assert call(_rows(L, 1, 0, 0), None, 0) == L.LSA_OK                            # no rows: nothing to do
+
+
 def test_attn_and_layer_validation(L):
     lib = L.lib()
     fake = ctypes.c_void_p(0x1000)

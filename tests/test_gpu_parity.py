@@ -462,6 +462,43 @@ def test_layer_bf16_decode_ragged():
         assert set(picks) <= set(g_idx[b].tolist())
 
 
+FUSED_LENGTHS = [1, 17, 1041, 1042, 3001, 8192, 8193, 20000, 40000, 200001]
+FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9, 8192 + 1040), (6, 8193), (5, 8192)]
+
+
+def test_layer_fused_first_level_equals_separate_passes():
+    # Rows scored one by one go through the fused scoring + first top-K level (segments of 8192
+    # columns; used when rows x segments >= 256, here 14 x 25); the index sets must be bit-identical to
+    # scoring everything and then selecting.
+    x = custom_rows(FUSED_LENGTHS, FUSED_ROWS, seed=41)
+    c = x["cfg"]
+    idx_layer = lsa.lsa_layer_fwd(c, rows_of(x), x["q"], x["kv"], q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])[0]
+    sc = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c))
+    idx_sep = lsa.lsa_topk(sc, c["k_sparse"])
+    assert torch.equal(idx_layer, idx_sep)
+    assert (host(idx_layer)[0] == -1).all()       # L = 1: no mid region
+
+
+@pytest.mark.parametrize("k", [1, 1024, 4096])
+def test_index_topk_equals_score_then_topk(k):
+    # lsa_index_topk on the fused pass (14 rows x 25 segments of 8192 columns) and on the separate
+    # passes (2 rows) against scoring everything and then selecting: bit-identical index sets
+    for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 42), ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
+        x = custom_rows(lengths, rows, attn=False, seed=seed)
+        c = x["cfg"]
+        bud = (c["k_sink"], c["k_swa"], k)
+        log(f"index_topk k={k} rows={len(rows)} max_len={x['max_len']}")
+        got = lsa.lsa_index_topk(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud)
+        sc = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud)
+        assert torch.equal(got, lsa.lsa_topk(sc, k))
+        # a reused workspace and output give the same answer
+        ws = lsa.lsa_index_topk_workspace(rows_of(x), x["q_idx"], k)
+        again = torch.full_like(got, 7)
+        lsa.lsa_index_topk(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud, idx=again, ws=ws)
+        lsa.lsa_index_topk(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud, idx=again, ws=ws)
+        assert torch.equal(got, again)
+
+
 def test_layer_deterministic():
     x = synth.decode_batch([5000, 12000], device=DEV, seed=6, needles=4)
     c = x["cfg"]

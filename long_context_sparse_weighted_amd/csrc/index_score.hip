@@ -397,6 +397,11 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
 // chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
 // (sel_key / sel_pos [row][chunk * k_sel ..], key 0 / position -1 padded), so the fp32 scores never go
 // to HBM (their write traffic, interleaved with the key stream, slowed the stream by ~15 % at 1M).
+// Slot of score i (0 <= i < 8192) in the fused kernel's LDS score buffer: each 32-float row is rotated
+// by its row index, so that the epilogue's reads (thread t takes scores 32 t .. 32 t + 31) hit 32
+// different banks instead of one, while the stream's writes of 64 consecutive scores stay conflict-free.
+__device__ inline int64_t fused_slot(int64_t i) { return (i & ~(int64_t)31) | ((i + (i >> 5)) & 31); }
+
 template <int MODE, int S, bool SELECT>
 __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                 const bool valid = key_of(tp, n) >= 0;
                 if (c < c_end) {
                     if constexpr (SELECT)
-                        sbuf[c - c_first] = valid ? v : -INFINITY;
+                        sbuf[fused_slot(c - c_first)] = valid ? v : -INFINITY;
                     else
                         out[c] = valid ? v : -INFINITY;
                 }
@@ -611,7 +616,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 #pragma unroll
         for (int m = 0; m < kV; ++m) {
             const int64_t c = c_first + kV * (int64_t)threadIdx.x + m;
-            const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[c - c_first] : -INFINITY;
+            const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[fused_slot(c - c_first)] : -INFINITY;
             key[m] = is_candidate(v) ? float_order_key(v) : 0u;
         }
         // The ring is free now: histograms, then the picks, and the selection's scalars after them.

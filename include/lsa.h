@@ -113,6 +113,20 @@ int lsa_index_score_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *
                         int64_t ld_scores, hipStream_t stream);
 
 /*
+ * The FP8 flat selection in one call: idx [n_rows, budget.k_sparse] receives exactly what lsa_topk
+ * (k = budget.k_sparse) returns for the flat scores of lsa_index_score_fp8 on the same inputs (pages ==
+ * NULL), bit for bit.  When rows x 8192-column chunks fill the chip, each block keeps its chunk's scores
+ * on chip and writes only its k best (score, position) pairs, as lsa_index_topk does for bf16.
+ * Arguments and errors as for lsa_index_score_fp8 and lsa_index_topk; 1 <= k_sparse <= 4096.
+ * Workspace: lsa_index_topk_fp8_workspace_size() bytes, 256-byte aligned.
+ */
+int lsa_index_topk_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q_scale, const float *w,
+                       const uint8_t *k8, const float *k_scale, int32_t n_heads, int32_t head_dim,
+                       lsa_budget_t budget, int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream);
+int lsa_index_topk_fp8_workspace_size(const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k_sparse,
+                                      size_t *bytes);
+
+/*
  * Sub-block mean cache of the indexer keys ([paper] §3.3 "Design choices": precomputed once per
  * sequence and cached).  Sub-block n of sequence b covers tokens [nB, min((n+1)B, L_b)); row
  * sb_off[b] + n of k_mean [sb_off[n_seq], head_dim] receives the mean over the tokens present,

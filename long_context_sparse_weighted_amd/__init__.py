@@ -18,7 +18,8 @@ LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = r
 LSA_F32, LSA_BF16 = 0, 1
 
 SYMBOLS = ("lsa_index_score", "lsa_quantize_fp8", "lsa_index_score_fp8", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
-           "lsa_topk_workspace_size", "lsa_index_topk", "lsa_index_topk_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
+           "lsa_topk_workspace_size", "lsa_index_topk", "lsa_index_topk_workspace_size",
+           "lsa_index_topk_fp8", "lsa_index_topk_fp8_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
            "lsa_layer_workspace_size", "lsa_status_string", "lsa_last_error")
 
 
@@ -68,6 +69,8 @@ def lib():
         L.lsa_topk_workspace_size.argtypes = [I32, I64, I32, ctypes.POINTER(SZ)]
         L.lsa_index_topk.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, P, SZ, P]
         L.lsa_index_topk_workspace_size.argtypes = [ctypes.c_int, RP, I32, I32, I32, ctypes.POINTER(SZ)]
+        L.lsa_index_topk_fp8.argtypes = [RP, P, P, P, P, P, I32, I32, Budget, P, P, SZ, P]
+        L.lsa_index_topk_fp8_workspace_size.argtypes = [RP, I32, I32, I32, ctypes.POINTER(SZ)]
         L.lsa_hybrid_attn.argtypes = [ctypes.c_int, RP, P, P, I32, I32, I32, F, Budget, P, P, P, P, P, SZ, P]
         L.lsa_hybrid_attn_workspace_size.argtypes = [ctypes.c_int, RP, I32, I32, Budget, ctypes.POINTER(SZ)]
         L.lsa_layer_fwd.argtypes = [ctypes.POINTER(LayerCfg), RP, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -272,6 +275,31 @@ def lsa_index_topk(rows: RowsDesc, q_idx, w, k_idx, budget, idx=None, ws=None):
         idx = torch.empty((n_rows, bud.k_sparse), dtype=torch.int32, device=q_idx.device)
     _check(lib().lsa_index_topk(dt, ctypes.byref(rows.c()), _p(q_idx), _p(w), _p(k_idx), HI, dI, bud, _p(idx), wp,
                                 wn, _stream()))
+    return idx
+
+
+def lsa_index_topk_fp8_workspace(rows: RowsDesc, q8, k_sparse):
+    """A workspace tensor for lsa_index_topk_fp8 on these rows."""
+    n_rows, HI, dI = q8.shape
+    sz = ctypes.c_size_t()
+    _check(lib().lsa_index_topk_fp8_workspace_size(ctypes.byref(rows.c()), HI, dI, int(k_sparse), ctypes.byref(sz)))
+    return _workspace(sz.value, q8.device)
+
+
+def lsa_index_topk_fp8(rows: RowsDesc, q8, q_scale, w, k8, k_scale, budget, idx=None, ws=None):
+    """idx [n_rows, k_sparse] int32: the FP8 flat token selection (scores and top-K in one call)."""
+    n_rows, HI, dI = q8.shape
+    for t, dt, name in ((q8, torch.uint8, "q8"), (k8, torch.uint8, "k8"), (q_scale, torch.float32, "q_scale"),
+                        (k_scale, torch.float32, "k_scale"), (w, torch.float32, "w")):
+        _need(t, dt, name)
+    bud = Budget(*budget)
+    if ws is None:
+        ws = lsa_index_topk_fp8_workspace(rows, q8, bud.k_sparse)
+    wp, wn = _aligned(ws)
+    if idx is None:
+        idx = torch.empty((n_rows, bud.k_sparse), dtype=torch.int32, device=q8.device)
+    _check(lib().lsa_index_topk_fp8(ctypes.byref(rows.c()), _p(q8), _p(q_scale), _p(w), _p(k8), _p(k_scale), HI, dI,
+                                    bud, _p(idx), wp, wn, _stream()))
     return idx
 
 

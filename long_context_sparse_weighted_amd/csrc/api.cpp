@@ -344,6 +344,91 @@ int lsa_index_score_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *
     return hip_status(e, "lsa_index_score_fp8 launch");
 }
 
+// FP8 flat selection: the fused pass when rows x 8192-column chunks fill the chip, else the FP8 scores
+// (first in the workspace) and the top-K levels over them.
+static bool fp8_fused(const lsa_rows_t *rows, int k)
+{
+    return k >= 1 && k <= 4096 && (int64_t)rows->n_rows * index_select_fused_segments(rows->max_kv_len) >= 256;
+}
+
+static size_t fp8_select_bytes(const lsa_rows_t *rows, int k, size_t *scores_bytes)
+{
+    const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
+    if (fp8_fused(rows, k)) {
+        *scores_bytes = 0;
+        return topk_lists_workspace_bytes(rows->n_rows, index_select_fused_segments(ld), k);
+    }
+    *scores_bytes = align_up(sizeof(float) * (size_t)rows->n_rows * (size_t)ld);
+    return *scores_bytes + topk_workspace_bytes(rows->n_rows, ld, k);
+}
+
+static int check_index_topk_fp8(const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k)
+{
+    if (int st = check_rows(rows))
+        return st;
+    if (n_heads != 64 || head_dim != 128)
+        return fail(LSA_ERR_UNSUPPORTED, "FP8 indexer compiled for 64 heads of dim 128 only (got %d, %d)", n_heads,
+                    head_dim);
+    if (k < 1 || k > 4096)
+        return fail(LSA_ERR_UNSUPPORTED, "k_sparse must be in [1, 4096]");
+    return LSA_OK;
+}
+
+int lsa_index_topk_fp8_workspace_size(const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k_sparse,
+                                      size_t *bytes)
+{
+    if (!bytes)
+        return fail(LSA_ERR_INVALID, "bytes is NULL");
+    if (int st = check_index_topk_fp8(rows, n_heads, head_dim, k_sparse))
+        return st;
+    size_t sb;
+    *bytes = fp8_select_bytes(rows, k_sparse, &sb);
+    return ok();
+}
+
+int lsa_index_topk_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q_scale, const float *w,
+                       const uint8_t *k8, const float *k_scale, int32_t n_heads, int32_t head_dim,
+                       lsa_budget_t budget, int32_t *idx, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (int st = check_index_topk_fp8(rows, n_heads, head_dim, budget.k_sparse))
+        return st;
+    if (int st = check_budget(budget))
+        return st;
+    if (rows->n_rows > 0 && (!q8 || !q_scale || !w || !k8 || !k_scale || !idx))
+        return fail(LSA_ERR_INVALID, "q8, q_scale, w, k8, k_scale and idx must be device pointers");
+    size_t sb;
+    const size_t need = fp8_select_bytes(rows, budget.k_sparse, &sb);
+    if (ws_bytes < need || (need && !ws))
+        return fail(LSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
+    if (ws && !aligned256(ws))
+        return fail(LSA_ERR_INVALID, "workspace must be 256-byte aligned");
+    if (rows->n_rows == 0)
+        return ok();
+    const RowsDev rd = to_dev(rows);
+    const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
+    const int k = budget.k_sparse;
+    hipError_t e;
+    if (fp8_fused(rows, k)) {
+        const int64_t n_seg = index_select_fused_segments(ld);
+        uint32_t *sk;
+        int32_t *sp;
+        int64_t sld;
+        topk_first_lists(ws, rows->n_rows, n_seg, k, &sk, &sp, &sld);
+        e = launch_index_select_fused_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, ld, k, sk, sp,
+                                          sld, stream);
+        if (e == hipSuccess)
+            e = launch_topk_lists(rows->n_rows, n_seg, k, ws, idx, RowGate{nullptr, 0}, stream);
+    } else {
+        float *scores = (float *)ws;
+        e = launch_index_score_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, nullptr, 0, 1, scores,
+                                   ld, stream);
+        if (e == hipSuccess)
+            e = launch_topk(rows->n_rows, scores, ld, ld, nullptr, 0, 1, k, idx, (char *)ws + sb, RowGate{nullptr, 0},
+                            stream);
+    }
+    return hip_status(e, "lsa_index_topk_fp8 launch");
+}
+
 int lsa_page_means(int dtype, int32_t n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,
                    int32_t head_dim, int32_t B, int64_t max_kv_len, int64_t first_token, void *k_mean,
                    hipStream_t stream)

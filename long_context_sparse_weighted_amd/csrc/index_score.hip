@@ -402,6 +402,44 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
 // different banks instead of one, while the stream's writes of 64 consecutive scores stay conflict-free.
 __device__ inline int64_t fused_slot(int64_t i) { return (i & ~(int64_t)31) | ((i + (i >> 5)) & 31); }
 
+// Epilogue of the fused scoring kernels: the block's 8192 scores (columns c_first ..; only
+// [c_begin, c_end) hold scores, the rest count as -inf) are in sbuf; select the k_sel best under
+// (score desc, position asc) with the block radix select, using the block's (now idle) ring LDS at lds
+// (kLdsWords + 16 words), and write them as (order key, position) pairs at chunk * k_sel of row r's
+// candidate list, padded with (0, -1).
+__device__ inline void fused_select_epilogue(const float *sbuf, uint32_t *lds, bool empty, int64_t c_first,
+                                             int64_t c_begin, int64_t c_end, int r, int64_t chunk, int k_sel,
+                                             uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
+                                             int64_t sel_ld)
+{
+    __syncthreads();  // every wave's scores are in sbuf, every wave's ring DMA has landed
+    // Keys of the chunk: thread t takes columns c_first + 32 t .. + 31 (position order).
+    constexpr int kV = kFusedCols / 256;
+    uint32_t key[kV];
+#pragma unroll
+    for (int m = 0; m < kV; ++m) {
+        const int64_t c = c_first + kV * (int64_t)threadIdx.x + m;
+        const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[fused_slot(c - c_first)] : -INFINITY;
+        key[m] = is_candidate(v) ? float_order_key(v) : 0u;
+    }
+    // Histograms, then the picks, and the selection's scalars after them.
+    uint32_t *scratch = lds + kLdsWords;
+    int *s_d = reinterpret_cast<int *>(scratch + 12);
+    uint32_t *s_above = scratch + 13, *s_bin = scratch + 14;
+    const Selection sel = block_select<256, kV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
+    uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
+    __syncthreads();
+    const uint32_t n_sel = block_emit<256, kV>(key, sel, scratch, stage_key, stage_li, (uint32_t)(kV * threadIdx.x));
+    __syncthreads();
+    uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
+    int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
+    for (int i = threadIdx.x; i < k_sel; i += blockDim.x) {
+        const bool ok = (uint32_t)i < n_sel;
+        kout[i] = ok ? stage_key[i] : 0u;
+        pout[i] = ok ? (int32_t)(c_first + stage_li[i]) : -1;
+    }
+}
+
 template <int MODE, int S, bool SELECT>
 __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
@@ -608,36 +646,9 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
         }
     }
-    if constexpr (SELECT) {
-        __syncthreads();  // every wave's scores are in sbuf, every wave's ring DMA has landed
-        // Keys of the chunk: thread t takes columns c_first + 32 t .. + 31 (position order).
-        constexpr int kV = kFusedCols / 256;
-        uint32_t key[kV];
-#pragma unroll
-        for (int m = 0; m < kV; ++m) {
-            const int64_t c = c_first + kV * (int64_t)threadIdx.x + m;
-            const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[fused_slot(c - c_first)] : -INFINITY;
-            key[m] = is_candidate(v) ? float_order_key(v) : 0u;
-        }
-        // The ring is free now: histograms, then the picks, and the selection's scalars after them.
-        uint32_t *lds = reinterpret_cast<uint32_t *>(&ring[0][0][0]);
-        uint32_t *scratch = lds + kLdsWords;
-        int *s_d = reinterpret_cast<int *>(scratch + 12);
-        uint32_t *s_above = scratch + 13, *s_bin = scratch + 14;
-        const Selection sel = block_select<256, kV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
-        uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
-        __syncthreads();
-        const uint32_t n_sel = block_emit<256, kV>(key, sel, scratch, stage_key, stage_li,
-                                                   (uint32_t)(kV * threadIdx.x));
-        __syncthreads();
-        uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
-        int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
-        for (int i = threadIdx.x; i < k_sel; i += blockDim.x) {
-            const bool ok = (uint32_t)i < n_sel;
-            kout[i] = ok ? stage_key[i] : 0u;
-            pout[i] = ok ? (int32_t)(c_first + stage_li[i]) : -1;
-        }
-    }
+    if constexpr (SELECT)
+        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), empty, c_first, c_begin, c_end, r,
+                              chunk, k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -682,20 +693,24 @@ __device__ inline void dma_4(const void *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
-template <int MODE, int S>
+template <int MODE, int S, bool SELECT>
 __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
                                                          const float *__restrict__ q_scale,
                                                          const float *__restrict__ w, const uint8_t *__restrict__ k8,
                                                          const float *__restrict__ k_scale, int k_sink, int k_swa,
                                                          const int32_t *__restrict__ pages, int M, int P,
                                                          float *__restrict__ scores, int64_t ld, int64_t n_cols,
-                                                         int64_t cols_per_block)
+                                                         int64_t cols_per_block, int k_sel, uint32_t *__restrict__ sel_key,
+                                                         int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * (kLdsWords + 16)),
+                  "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
     stream_block<MODE>(r, chunk);
     __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
+    __shared__ __attribute__((aligned(16))) float sbuf[SELECT ? kFusedCols : 1];  // SELECT: the chunk's scores
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -709,15 +724,22 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
     float *out = scores + (int64_t)r * ld;
     int64_t c_begin, c_end;
     chunk_key_range<MODE>(cm, c_first, c_last, c_begin, c_end);
-    if (cm.lo >= cm.hi || c_begin >= c_end) {
-        for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
+    const bool empty = cm.lo >= cm.hi || c_begin >= c_end;
+    if constexpr (!SELECT) {
+        if (empty) {
+            for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
+                out[c] = -INFINITY;
+            return;
+        }
+        for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
             out[c] = -INFINITY;
+        for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
+            out[c] = -INFINITY;
+    } else if (empty) {  // no keys here: publish the empty candidate list
+        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), true, c_first, c_begin, c_end, r,
+                              chunk, k_sel, sel_key, sel_pos, sel_ld);
         return;
     }
-    for (int64_t c = c_first + threadIdx.x; c < c_begin; c += blockDim.x)
-        out[c] = -INFINITY;
-    for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
-        out[c] = -INFINITY;
     // A operand of head block mt: lane (n, g) holds bytes 32 g .. 32 g + 31 of head 16 mt + n; the key
     // operand uses the same byte split, so the product is the full 128-byte dot product.
     i32x8 qa[4];
@@ -849,22 +871,29 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
             const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
             const int64_t c = tile_of(k0 + g) * kTile + n;
             const bool valid = key_of(tp, n) >= 0;
-            if (c < c_end)
-                out[c] = valid ? v : -INFINITY;
+            if (c < c_end) {
+                if constexpr (SELECT)
+                    sbuf[fused_slot(c - c_first)] = valid ? v : -INFINITY;
+                else
+                    out[c] = valid ? v : -INFINITY;
+            }
         }
         wait_vmcnt<0>();
     }
+    if constexpr (SELECT)
+        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), false, c_first, c_begin, c_end, r,
+                              chunk, k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)
-template __global__ void score_fp8_kernel<kModeFlat, kFp8Ring>(RowsDev, const uint8_t *, const float *, const float *,
-                                                                 const uint8_t *, const float *, int, int,
-                                                                 const int32_t *, int, int, float *, int64_t, int64_t,
-                                                                 int64_t);
-template __global__ void score_fp8_kernel<kModePaged, kFp8Ring>(RowsDev, const uint8_t *, const float *, const float *,
-                                                                  const uint8_t *, const float *, int, int,
-                                                                  const int32_t *, int, int, float *, int64_t, int64_t,
-                                                                  int64_t);
+#define LSA_FP8_INSTANCE(MODE, SEL)                                                                                 \
+    template __global__ void score_fp8_kernel<MODE, kFp8Ring, SEL>(                                                    \
+        RowsDev, const uint8_t *, const float *, const float *, const uint8_t *, const float *, int, int,             \
+        const int32_t *, int, int, float *, int64_t, int64_t, int64_t, int, uint32_t *, int32_t *, int64_t);
+LSA_FP8_INSTANCE(kModeFlat, false)
+LSA_FP8_INSTANCE(kModePaged, false)
+LSA_FP8_INSTANCE(kModeFlat, true)
+#undef LSA_FP8_INSTANCE
 
 // ------------------------------------------------------------------------------------------
 // Multi-row bf16 kernel (prefill): the 16 rows of a group share every key tile, so the keys are read
@@ -1319,11 +1348,27 @@ hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const 
     const ScoreGeom geo = score_geometry(rows.n_rows, ld, LSA_FP8_BLOCKS_PER_CU);
     dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
     if (pages)
-        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring>), grid, dim3(256), 0, stream, rows, q8, q_scale, w,
-                           k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems);
+        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring, false>), grid, dim3(256), 0, stream, rows, q8,
+                           q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
+                           nullptr, nullptr, (int64_t)0);
     else
-        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring>), grid, dim3(256), 0, stream, rows, q8, q_scale, w,
-                           k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems);
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, false>), grid, dim3(256), 0, stream, rows, q8,
+                           q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
+                           nullptr, nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_select_fused_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,
+                                         const uint8_t *k8, const float *k_scale, int k_sink, int k_swa,
+                                         int64_t n_cols, int k, uint32_t *sel_key, int32_t *sel_pos, int64_t sel_ld,
+                                         hipStream_t stream)
+{
+    if (rows.n_rows == 0 || n_cols == 0)
+        return hipSuccess;
+    dim3 grid((unsigned)index_select_fused_segments(n_cols), (unsigned)rows.n_rows);
+    hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, true>), grid, dim3(256), 0, stream, rows, q8, q_scale,
+                       w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols, (int64_t)kFusedCols,
+                       k, sel_key, sel_pos, sel_ld);
     return hipGetLastError();
 }
 

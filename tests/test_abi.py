@@ -166,6 +166,33 @@ def test_index_topk_validation_and_workspace(L):
     assert call(_rows(L, 1, 0, 0), None, 0) == L.LSA_OK                            # no rows: nothing to do
 
 
+def test_index_topk_fp8_validation_and_workspace(L):
+    lib = L.lib()
+    fake = ctypes.c_void_p(0x1000)
+    b = L.Budget(16, 1024, 1024)
+    sz = ctypes.c_size_t()
+    big = _rows(L, 32, 32, 1 << 20)
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(big), 64, 128, 1024, ctypes.byref(sz)) == L.LSA_OK
+    assert 0 < sz.value < 32 * (1 << 20) * 4 // 3      # candidate lists, no score matrix
+    small = _rows(L, 1, 1, 20000)
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(small), 64, 128, 1024, ctypes.byref(sz)) == L.LSA_OK
+    assert sz.value >= 20000 * 4
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(big), 32, 128, 1024, ctypes.byref(sz)) == \
+        L.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(big), 64, 128, 0, ctypes.byref(sz)) == \
+        L.LSA_ERR_UNSUPPORTED
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(big), 64, 128, 1024, None) == L.LSA_ERR_INVALID
+    assert lib.lsa_index_topk_fp8_workspace_size(ctypes.byref(big), 64, 128, 1024, ctypes.byref(sz)) == L.LSA_OK
+    call = lambda ws, n, k8=fake, bud=b: lib.lsa_index_topk_fp8(ctypes.byref(big), fake, fake, fake, k8, fake, 64, 128,
+                                                               bud, fake, ws, n, None)
+    assert call(fake, sz.value - 1) == L.LSA_ERR_WORKSPACE
+    assert call(fake, sz.value, k8=None) == L.LSA_ERR_INVALID
+    assert call(ctypes.c_void_p(0x1010), sz.value) == L.LSA_ERR_INVALID          # not 256-byte aligned
+    assert call(fake, sz.value, bud=L.Budget(16, -1, 1024)) == L.LSA_ERR_INVALID
+    assert lib.lsa_index_topk_fp8(ctypes.byref(_rows(L, 1, 0, 0)), None, None, None, None, None, 64, 128, b, None,
+                                  None, 0, None) == L.LSA_OK
+
+
 def test_attn_and_layer_validation(L):
     lib = L.lib()
     fake = ctypes.c_void_p(0x1000)

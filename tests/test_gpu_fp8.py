@@ -12,7 +12,7 @@ import synth
 from oracle import fp8
 from parity_util import (assert_idx_sets_match, assert_scores_close, budget_of, f64, host, kth_best, log, near_tie,
                          oracle_inputs, rows_of)
-from test_gpu_parity import RAGGED_LENGTHS, RAGGED_ROWS, custom_rows
+from test_gpu_parity import FUSED_LENGTHS, FUSED_ROWS, RAGGED_LENGTHS, RAGGED_ROWS, custom_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -114,3 +114,18 @@ def test_fp8_selection_vs_oracle():
     log(f"fp8 selection: {n} rows with near-tie differences")
     for b, picks in enumerate(x["needles"]):
         assert set(picks) <= set(g_idx[b].tolist())
+
+
+@pytest.mark.parametrize("k", [1, 1024, 4096])
+def test_index_topk_fp8_equals_score_then_topk(k):
+    # the fused FP8 pass (14 rows x 25 segments of 8192 columns) and the separate passes (2 rows) against
+    # FP8 scores then top-K: bit-identical index sets
+    for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 44), ([20000, 9000], [(0, 19999), (1, 8999)], 45)):
+        x = custom_rows(lengths, rows, attn=False, seed=seed)
+        c = x["cfg"]
+        bud = (c["k_sink"], c["k_swa"], k)
+        log(f"index_topk_fp8 k={k} rows={len(rows)} max_len={x['max_len']}")
+        q8, qs, k8, ks = _gpu_fp8(x)
+        got = lsa.lsa_index_topk_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
+        sc = lsa.lsa_index_score_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
+        assert torch.equal(got, lsa.lsa_topk(sc, k))

@@ -332,10 +332,10 @@ __device__ inline void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Fused scoring + first top-K level (decode): columns per block, ring depth (3 x 16 KB per block, then
-// reused by the selection) and 32 KB of staged scores: 80 KB, two blocks per CU.
+// Fused scoring + first top-K level (decode): columns per block and ring depth (5 x 16 KB per block,
+// reused by the selection; the scores stay in registers): 80 KB, two blocks per CU.
 constexpr int kFusedCols = 8192;
-constexpr int kFusedRing = 3;
+constexpr int kFusedRing = 5;
 
 // Block -> (row, chunk) of the streaming kernels.  Blocks go to the 8 XCDs in turn, in launch order
 // (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  A paged row's chunks can
@@ -397,46 +397,76 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
 // chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
 // (sel_key / sel_pos [row][chunk * k_sel ..], key 0 / position -1 padded), so the fp32 scores never go
 // to HBM (their write traffic, interleaved with the key stream, slowed the stream by ~15 % at 1M).
-// Slot of score i (0 <= i < 8192) in the fused kernel's LDS score buffer: each 32-float row is rotated
-// by its row index, so that the epilogue's reads (thread t takes scores 32 t .. 32 t + 31) hit 32
-// different banks instead of one, while the stream's writes of 64 consecutive scores stay conflict-free.
-__device__ inline int64_t fused_slot(int64_t i) { return (i & ~(int64_t)31) | ((i + (i >> 5)) & 31); }
+constexpr int kFusedV = kFusedCols / 256;                            // scores per thread (32)
+constexpr int kFusedLdsWords = kFusedCols + 2 * (kFusedCols / 32) + 16;  // keys by position, 2 bit maps, scan
 
-// Epilogue of the fused scoring kernels: the block's 8192 scores (columns c_first ..; only
-// [c_begin, c_end) hold scores, the rest count as -inf) are in sbuf; select the k_sel best under
-// (score desc, position asc) with the block radix select, using the block's (now idle) ring LDS at lds
-// (kLdsWords + 16 words), and write them as (order key, position) pairs at chunk * k_sel of row r's
-// candidate list, padded with (0, -1).
-__device__ inline void fused_select_epilogue(const float *sbuf, uint32_t *lds, bool empty, int64_t c_first,
-                                             int64_t c_begin, int64_t c_end, int r, int64_t chunk, int k_sel,
-                                             uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
-                                             int64_t sel_ld)
+// Epilogue of the fused scoring kernels, on scores held in registers: thread (wave w, lane (g, n)) holds
+// in s[j] the score of column (tile0 + 4 (4 j + w) + g) * 16 + n, i.e. of its j-th group of four tiles
+// (-inf where that column holds no key or lies past the chunk's key range).  Selects the k_sel best
+// under (score desc, position asc) with the block radix select, then writes them in position order:
+// every pick is put at its position in an LDS array and flagged in a bit map over the chunk's 8192
+// columns (ties at the threshold in a second map, ranked by a scan over the map's words), and thread t
+// emits the picks of columns 32 t .. 32 t + 31.  The pairs (order key, position) go to chunk * k_sel
+// of row r's candidate list, padded with (0, -1).  lds: the block's idle ring, kFusedLdsWords words.
+__device__ inline void fused_select_regs(const float (&s)[kFusedV], uint32_t *lds, int64_t c_first, int64_t tile0,
+                                         int wave, int g, int n, int r, int64_t chunk, int k_sel,
+                                         uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
+                                         int64_t sel_ld)
 {
-    __syncthreads();  // every wave's scores are in sbuf, every wave's ring DMA has landed
-    // Keys of the chunk: thread t takes columns c_first + 32 t .. + 31 (position order).
-    constexpr int kV = kFusedCols / 256;
-    uint32_t key[kV];
+    static_assert(kLdsWords + 16 <= kFusedLdsWords && kFusedCols / 32 == 256, "one bit-map word per thread");
+    __syncthreads();  // every wave's ring DMA has landed: the ring's LDS is free
+    uint32_t key[kFusedV];
 #pragma unroll
-    for (int m = 0; m < kV; ++m) {
-        const int64_t c = c_first + kV * (int64_t)threadIdx.x + m;
-        const float v = (!empty && c >= c_begin && c < c_end) ? sbuf[fused_slot(c - c_first)] : -INFINITY;
-        key[m] = is_candidate(v) ? float_order_key(v) : 0u;
-    }
-    // Histograms, then the picks, and the selection's scalars after them.
+    for (int m = 0; m < kFusedV; ++m)
+        key[m] = is_candidate(s[m]) ? float_order_key(s[m]) : 0u;
     uint32_t *scratch = lds + kLdsWords;
     int *s_d = reinterpret_cast<int *>(scratch + 12);
     uint32_t *s_above = scratch + 13, *s_bin = scratch + 14;
-    const Selection sel = block_select<256, kV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
-    uint32_t *stage_key = lds, *stage_li = lds + kMaxLocalK + kWave;
+    const Selection sel = block_select<256, kFusedV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
+    // Thresholds on the whole key (as in block_emit): picked when x >= t_gt; a tie when x == t_eq.
+    uint32_t t_gt, t_eq = 0xffffffffu;
+    if (sel.all)
+        t_gt = 1u;
+    else if (sel.whole)
+        t_gt = sel.prefix << (32 - sel.consumed);
+    else
+        t_gt = sel.prefix + 1u, t_eq = sel.prefix;
+    uint32_t *pkey = lds, *gmap = lds + kFusedCols, *emap = gmap + kFusedCols / 32, *scan = emap + kFusedCols / 32;
+    __syncthreads();  // the selection's LDS is no longer read
+    gmap[threadIdx.x] = 0u;
+    emap[threadIdx.x] = 0u;
     __syncthreads();
-    const uint32_t n_sel = block_emit<256, kV>(key, sel, scratch, stage_key, stage_li, (uint32_t)(kV * threadIdx.x));
+#pragma unroll
+    for (int m = 0; m < kFusedV; ++m) {
+        const uint32_t x = key[m];
+        if (x >= t_gt || x == t_eq) {  // a candidate (key 0 never is): its column lies in the chunk
+            const uint32_t li = (uint32_t)((tile0 + 4 * (m * kWavesPerBlock + wave) + g) * kTile + n - c_first);
+            pkey[li] = x;
+            atomicOr(x >= t_gt ? &gmap[li >> 5] : &emap[li >> 5], 1u << (li & 31));
+        }
+    }
     __syncthreads();
+    const uint32_t gw = gmap[threadIdx.x], ew = emap[threadIdx.x];
+    uint32_t bg, be, tg, te;
+    block_scan2<256>((uint32_t)__popc(gw), (uint32_t)__popc(ew), bg, be, tg, te, scan);
     uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
     int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
-    for (int i = threadIdx.x; i < k_sel; i += blockDim.x) {
-        const bool ok = (uint32_t)i < n_sel;
-        kout[i] = ok ? stage_key[i] : 0u;
-        pout[i] = ok ? (int32_t)(c_first + stage_li[i]) : -1;
+    uint32_t slot = bg + (be < sel.k_rem ? be : sel.k_rem);  // picks at lower positions
+    uint32_t e_seen = be;
+    for (int b = 0; b < 32; ++b) {
+        const bool gb = (gw >> b) & 1u, eb = (ew >> b) & 1u;
+        if (gb || (eb && e_seen < sel.k_rem)) {
+            const uint32_t li = 32u * threadIdx.x + (uint32_t)b;
+            kout[slot] = pkey[li];
+            pout[slot] = (int32_t)(c_first + li);
+            ++slot;
+        }
+        e_seen += eb ? 1u : 0u;
+    }
+    const uint32_t n_sel = tg + (te < sel.k_rem ? te : sel.k_rem);
+    for (uint32_t i = n_sel + threadIdx.x; i < (uint32_t)k_sel; i += blockDim.x) {
+        kout[i] = 0u;
+        pout[i] = -1;
     }
 }
 
@@ -451,7 +481,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * (kLdsWords + 16)),
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * kFusedLdsWords),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
@@ -461,7 +491,6 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
         return;  // scored by the multi-row kernel
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
-    __shared__ __attribute__((aligned(16))) float sbuf[SELECT ? kFusedCols : 1];  // SELECT: the chunk's scores
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -488,6 +517,12 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     }
+    // SELECT: this lane's scores, one per group of four tiles (see fused_select_regs)
+    float sreg[SELECT ? kFusedV : 1];
+#pragma unroll
+    for (int m = 0; m < (SELECT ? kFusedV : 1); ++m)
+        sreg[m] = -INFINITY;
+    int64_t sel_tile0 = 0;
     if (!empty) {  // (SELECT: a block without keys still publishes its empty candidate list below)
         u32x4 qa[4][4];
         const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
@@ -529,6 +564,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         auto tile_of = [&](int64_t k) __attribute__((always_inline)) -> int64_t {
             return chunk_tile + 4 * ((k >> 2) * W + wave) + (k & 3);
         };
+        sel_tile0 = chunk_tile;
         const int64_t safe_key = cm.base + cm.lo;
         const uint32_t ring_base =
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&ring[0][wave][0];
@@ -621,34 +657,56 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             }
             return v;
         };
+        // Group k0 / 4 (tiles k0 .. k0 + 3): lane group g takes tile g's 16 scores (-inf past c_end or
+        // where a column holds no key).
+        auto group = [&](int64_t k0, int64_t &c) __attribute__((always_inline)) -> float {
+            const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
+            const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
+            const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
+            const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
+            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+            const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
+            c = tile_of(k0 + g) * kTile + n;
+            return c < c_end && key_of(tp, n) >= 0 ? v : -INFINITY;
+        };
         if (K > 0) {
             for (int k = 0; k < S; ++k)
                 issue(k);
-            // Groups of 4 tiles: lane group g stores tile g's 16 scores, so one store instruction writes
-            // 256 contiguous bytes (whole lines).  The DMA waits above count DMA instructions only: a
-            // store between the DMA of a tile and its wait only makes the wait stricter.
-            for (int64_t k0 = 0; k0 < K; k0 += 4) {
-                const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
-                const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
-                const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
-                const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-                const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
-                const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
-                const int64_t c = tile_of(k0 + g) * kTile + n;
-                const bool valid = key_of(tp, n) >= 0;
-                if (c < c_end) {
-                    if constexpr (SELECT)
-                        sbuf[fused_slot(c - c_first)] = valid ? v : -INFINITY;
-                    else
-                        out[c] = valid ? v : -INFINITY;
+            if constexpr (SELECT) {
+                // The scores stay in registers: groups in runs of 8 (register indices fixed at compile
+                // time), each run copied to its place in sreg by a wave-uniform branch.
+                for (int64_t j0 = 0; 4 * j0 < K; j0 += 8) {
+                    float part[8];
+    #pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        int64_t c;
+                        part[jj] = 4 * (j0 + jj) < K ? group(4 * (j0 + jj), c) : -INFINITY;
+                    }
+    #pragma unroll
+                    for (int o = 0; o < kFusedV / 8; ++o)
+                        if (j0 == 8 * o) {
+    #pragma unroll
+                            for (int jj = 0; jj < 8; ++jj)
+                                sreg[8 * o + jj] = part[jj];
+                        }
+                }
+            } else {
+                // Lane group g stores tile g's 16 scores, so one store instruction writes 256 contiguous
+                // bytes (whole lines).  The DMA waits above count DMA instructions only: a store between
+                // the DMA of a tile and its wait only makes the wait stricter.
+                for (int64_t k0 = 0; k0 < K; k0 += 4) {
+                    int64_t c;
+                    const float v = group(k0, c);
+                    if (c < c_end)
+                        out[c] = v;
                 }
             }
             wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
         }
     }
     if constexpr (SELECT)
-        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), empty, c_first, c_begin, c_end, r,
-                              chunk, k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r, chunk,
+                          k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -704,13 +762,16 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
                                                          int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * (kLdsWords + 16)),
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * kFusedLdsWords),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
     stream_block<MODE>(r, chunk);
     __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
-    __shared__ __attribute__((aligned(16))) float sbuf[SELECT ? kFusedCols : 1];  // SELECT: the chunk's scores
+    float sreg[SELECT ? kFusedV : 1];  // SELECT: this lane's scores, one per group of four tiles
+#pragma unroll
+    for (int m = 0; m < (SELECT ? kFusedV : 1); ++m)
+        sreg[m] = -INFINITY;
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -736,8 +797,8 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     } else if (empty) {  // no keys here: publish the empty candidate list
-        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), true, c_first, c_begin, c_end, r,
-                              chunk, k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
+                          sel_key, sel_pos, sel_ld);
         return;
     }
     // A operand of head block mt: lane (n, g) holds bytes 32 g .. 32 g + 31 of head 16 mt + n; the key
@@ -859,30 +920,51 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         }
         return v;
     };
+    // Group k0 / 4 (tiles k0 .. k0 + 3): lane group g takes tile g's 16 scores (-inf past c_end or
+    // where a column holds no key).
+    auto group = [&](int64_t k0, int64_t &c) __attribute__((always_inline)) -> float {
+        const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
+        const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
+        const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
+        const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
+        const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+        const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
+        c = tile_of(k0 + g) * kTile + n;
+        return c < c_end && key_of(tp, n) >= 0 ? v : -INFINITY;
+    };
     if (K > 0) {
         for (int k = 0; k < S; ++k)
             issue(k);
-        for (int64_t k0 = 0; k0 < K; k0 += 4) {
-            const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
-            const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
-            const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
-            const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
-            const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
-            const int64_t c = tile_of(k0 + g) * kTile + n;
-            const bool valid = key_of(tp, n) >= 0;
-            if (c < c_end) {
-                if constexpr (SELECT)
-                    sbuf[fused_slot(c - c_first)] = valid ? v : -INFINITY;
-                else
-                    out[c] = valid ? v : -INFINITY;
+        if constexpr (SELECT) {
+            // The scores stay in registers (as in the bf16 fused kernel).
+            for (int64_t j0 = 0; 4 * j0 < K; j0 += 8) {
+                float part[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    int64_t c;
+                    part[jj] = 4 * (j0 + jj) < K ? group(4 * (j0 + jj), c) : -INFINITY;
+                }
+#pragma unroll
+                for (int o = 0; o < kFusedV / 8; ++o)
+                    if (j0 == 8 * o) {
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj)
+                            sreg[8 * o + jj] = part[jj];
+                    }
+            }
+        } else {
+            for (int64_t k0 = 0; k0 < K; k0 += 4) {
+                int64_t c;
+                const float v = group(k0, c);
+                if (c < c_end)
+                    out[c] = v;
             }
         }
         wait_vmcnt<0>();
     }
     if constexpr (SELECT)
-        fused_select_epilogue(sbuf, reinterpret_cast<uint32_t *>(&ring[0][0][0]), false, c_first, c_begin, c_end, r,
-                              chunk, k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
+                          k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)

@@ -129,3 +129,17 @@ def test_index_topk_fp8_equals_score_then_topk(k):
         got = lsa.lsa_index_topk_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
         sc = lsa.lsa_index_score_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
         assert torch.equal(got, lsa.lsa_topk(sc, k))
+
+
+def test_index_topk_fp8_fused_ties():
+    # keys from 3 distinct vectors: long runs of equal FP8 scores, picks at the threshold by position
+    x = custom_rows(FUSED_LENGTHS, FUSED_ROWS, attn=False, seed=48)
+    n_tok = x["k_idx"].shape[0]
+    pick = torch.randint(0, 3, (n_tok,), generator=synth.generator(49, DEV), device=DEV)
+    x["k_idx"] = x["k_idx"][:3].clone()[pick].contiguous()
+    c = x["cfg"]
+    bud = (c["k_sink"], c["k_swa"], c["k_sparse"])
+    q8, qs, k8, ks = _gpu_fp8(x)
+    got = lsa.lsa_index_topk_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
+    sc = lsa.lsa_index_score_fp8(rows_of(x), q8, qs, x["w"], k8, ks, bud)
+    assert torch.equal(got, lsa.lsa_topk(sc, c["k_sparse"]))

@@ -466,6 +466,24 @@ FUSED_LENGTHS = [1, 17, 1041, 1042, 3001, 8192, 8193, 20000, 40000, 200001]
 FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9, 8192 + 1040), (6, 8193), (5, 8192)]
 
 
+@pytest.mark.parametrize("distinct", [1, 3, 40])
+def test_index_topk_fused_ties(distinct):
+    # keys drawn from a few distinct vectors, so every row's scores tie in long runs and the picks at the
+    # threshold are decided by position (1: all candidates equal); the fused pass (14 rows x 25
+    # segments) must match scoring then selecting bit for bit
+    x = custom_rows(FUSED_LENGTHS, FUSED_ROWS, attn=False, seed=46)
+    n_tok = x["k_idx"].shape[0]
+    pick = torch.randint(0, distinct, (n_tok,), generator=synth.generator(47, DEV), device=DEV)
+    x["k_idx"] = x["k_idx"][:distinct].clone()[pick].contiguous()
+    c = x["cfg"]
+    for k in (1, 1024):
+        bud = (c["k_sink"], c["k_swa"], k)
+        log(f"index_topk ties distinct={distinct} k={k}")
+        got = lsa.lsa_index_topk(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud)
+        sc = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], bud)
+        assert torch.equal(got, lsa.lsa_topk(sc, k))
+
+
 def test_layer_fused_first_level_equals_separate_passes():
     # Rows scored one by one go through the fused scoring + first top-K level (segments of 8192
     # columns; used when rows x segments >= 256, here 14 x 25); the index sets must be bit-identical to

@@ -497,7 +497,16 @@ __global__ __launch_bounds__(kT32, 1) void attn_mfma32_kernel(RowsDev rows, cons
                                                                uint16_t *__restrict__ out, float *__restrict__ lse,
                                                                AttnPartial part)
 {
-    const int split = blockIdx.x, r = blockIdx.y;
+    // Blocks go to the 8 XCDs in turn, in launch order.  When the rows come in multiples of 8, all the
+    // splits of a row go to one XCD: its q (147 KB, read by every split) then comes from that XCD's L2
+    // after the first split instead of from HBM once per split.
+    int split = blockIdx.x, r = blockIdx.y;
+    if (gridDim.z == 1 && gridDim.y % 8 == 0) {
+        const int id = blockIdx.x + gridDim.x * blockIdx.y;  // launch order
+        const int j = id >> 3;
+        r = (id & 7) + 8 * (j / (int)gridDim.x);
+        split = j % (int)gridDim.x;
+    }
     const int h_block = blockIdx.z * kH32;
     // Two K tiles as distinct objects, each named statically below (the DMA into one does not make
     // the compiler wait before reading the other), the P tile, the compacted picks.

@@ -116,11 +116,16 @@ def test_fp8_selection_vs_oracle():
         assert set(picks) <= set(g_idx[b].tolist())
 
 
+# The FP8 selection fuses from 1024 blocks (rows x 8192-column segments) on: 42 rows x 25 segments.
+FP8_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
+
+
 @pytest.mark.parametrize("k", [1, 1024, 4096])
 def test_index_topk_fp8_equals_score_then_topk(k):
-    # the fused FP8 pass (14 rows x 25 segments of 8192 columns) and the separate passes (2 rows) against
-    # FP8 scores then top-K: bit-identical index sets
-    for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 44), ([20000, 9000], [(0, 19999), (1, 8999)], 45)):
+    # the fused FP8 pass (42 rows x 25 segments of 8192 columns) and the separate passes (14 rows, 2 rows)
+    # against FP8 scores then top-K: bit-identical index sets
+    for lengths, rows, seed in ((FUSED_LENGTHS, FP8_FUSED_ROWS, 44), (FUSED_LENGTHS, FUSED_ROWS, 50),
+                                ([20000, 9000], [(0, 19999), (1, 8999)], 45)):
         x = custom_rows(lengths, rows, attn=False, seed=seed)
         c = x["cfg"]
         bud = (c["k_sink"], c["k_swa"], k)
@@ -133,7 +138,7 @@ def test_index_topk_fp8_equals_score_then_topk(k):
 
 def test_index_topk_fp8_fused_ties():
     # keys from 3 distinct vectors: long runs of equal FP8 scores, picks at the threshold by position
-    x = custom_rows(FUSED_LENGTHS, FUSED_ROWS, attn=False, seed=48)
+    x = custom_rows(FUSED_LENGTHS, FP8_FUSED_ROWS, attn=False, seed=48)
     n_tok = x["k_idx"].shape[0]
     pick = torch.randint(0, 3, (n_tok,), generator=synth.generator(49, DEV), device=DEV)
     x["k_idx"] = x["k_idx"][:3].clone()[pick].contiguous()

@@ -463,6 +463,7 @@ def test_layer_bf16_decode_ragged():
 
 
 FUSED_LENGTHS = [1, 17, 1041, 1042, 3001, 8192, 8193, 20000, 40000, 200001]
+# (the last two rows sit at t = L_b: rows outside their sequence, which select nothing)
 FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9, 8192 + 1040), (6, 8193), (5, 8192)]
 
 

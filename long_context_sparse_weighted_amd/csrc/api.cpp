@@ -344,13 +344,12 @@ int lsa_index_score_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *
     return hip_status(e, "lsa_index_score_fp8 launch");
 }
 
-// FP8 flat selection: the fused pass when rows x 8192-column chunks fill the chip several times over,
-// else the FP8 scores (first in the workspace) and the top-K levels over them.  The FP8 stream is twice
-// as fast per key as the bf16 one, so the selection epilogue weighs more: with a single round of blocks
-// (a 32-row batch at 128K: 512 blocks) the separate passes are faster (117.7 against 121.5 us).
+// FP8 flat selection: the fused pass when rows x 8192-column chunks fill the chip, else the FP8 scores
+// (first in the workspace) and the top-K levels over them.  (At 128K with 32 rows, a single round of
+// 512 blocks, the fused pass still wins: 121.5 against 130.2 us for the separate passes.)
 static bool fp8_fused(const lsa_rows_t *rows, int k)
 {
-    return k >= 1 && k <= 4096 && (int64_t)rows->n_rows * index_select_fused_segments(rows->max_kv_len) >= 1024;
+    return k >= 1 && k <= 4096 && (int64_t)rows->n_rows * index_select_fused_segments(rows->max_kv_len) >= 256;
 }
 
 static size_t fp8_select_bytes(const lsa_rows_t *rows, int k, size_t *scores_bytes)

@@ -116,13 +116,13 @@ def test_fp8_selection_vs_oracle():
         assert set(picks) <= set(g_idx[b].tolist())
 
 
-# The FP8 selection fuses from 1024 blocks (rows x 8192-column segments) on: 42 rows x 25 segments.
+# A larger fused batch than FUSED_ROWS: 42 rows x 25 segments of 8192 columns.
 FP8_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
 
 
 @pytest.mark.parametrize("k", [1, 1024, 4096])
 def test_index_topk_fp8_equals_score_then_topk(k):
-    # the fused FP8 pass (42 rows x 25 segments of 8192 columns) and the separate passes (14 rows, 2 rows)
+    # the fused FP8 pass (42 and 14 rows x 25 segments of 8192 columns) and the separate passes (2 rows)
     # against FP8 scores then top-K: bit-identical index sets
     for lengths, rows, seed in ((FUSED_LENGTHS, FP8_FUSED_ROWS, 44), (FUSED_LENGTHS, FUSED_ROWS, 50),
                                 ([20000, 9000], [(0, 19999), (1, 8999)], 45)):

@@ -124,9 +124,9 @@ struct LayerWs {
     size_t bytes;
 };
 
-// The fused flat pass works on fixed chunks of columns per block: it needs rows that are scored one by
-// one, and enough chunks to give every CU at least one block (a 32-row batch from 64K columns on;
-// below that the separate passes, whose chunks shrink with the work, are faster).
+// The fused flat pass works on fixed chunks of columns per block (8192, or 16384 for long rows): it needs
+// rows that are scored one by one, and enough chunks to give every CU at least one block (a 32-row batch
+// from 64K columns on; below that the separate passes, whose chunks shrink with the work, are faster).
 bool flat_fused(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k)
 {
     return index_select_fusable(dtype, rows->n_rows, n_heads, head_dim, k) &&
@@ -137,6 +137,13 @@ bool flat_fused(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows)
     return flat_fused(cfg->dtype, rows, cfg->n_heads_idx, cfg->head_dim_idx, cfg->budget.k_sparse);
 }
 
+// Chunks of the fused pass over ld columns.
+int64_t flat_fused_segments(const lsa_rows_t *rows, int64_t ld, int64_t *cols)
+{
+    *cols = index_select_fused_cols(rows->n_rows, ld);
+    return (ld + *cols - 1) / *cols;
+}
+
 // Workspace of the flat selection (lsa_index_topk and the layer's flat rows): candidate lists of the
 // fused pass, or the scores and the top-K lists of the separate passes; the scores come first.
 size_t flat_select_bytes(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k, size_t *scores_bytes)
@@ -144,7 +151,8 @@ size_t flat_select_bytes(int dtype, const lsa_rows_t *rows, int n_heads, int hea
     const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
     if (flat_fused(dtype, rows, n_heads, head_dim, k)) {
         *scores_bytes = 0;
-        return topk_lists_workspace_bytes(rows->n_rows, index_select_fused_segments(ld), k);
+        int64_t cols;
+        return topk_lists_workspace_bytes(rows->n_rows, flat_fused_segments(rows, ld, &cols), k);
     }
     *scores_bytes = align_up(sizeof(float) * (size_t)rows->n_rows * (size_t)ld);
     return *scores_bytes + topk_workspace_bytes(rows->n_rows, ld, k);
@@ -158,13 +166,14 @@ hipError_t launch_flat_select(int dtype, const lsa_rows_t *rows, const void *q_i
     const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
     if (flat_fused(dtype, rows, n_heads, head_dim, bud.k_sparse)) {
         // scoring and the first top-K level in one pass; the scores never leave the chip
-        const int64_t n_seg = index_select_fused_segments(ld);
+        int64_t cols;
+        const int64_t n_seg = flat_fused_segments(rows, ld, &cols);
         uint32_t *sk;
         int32_t *sp;
         int64_t sld;
         topk_first_lists(ws, rows->n_rows, n_seg, bud.k_sparse, &sk, &sp, &sld);
-        hipError_t e = launch_index_select_fused(rd, q_idx, w, k_idx, bud.k_sink, bud.k_swa, ld, bud.k_sparse, sk, sp,
-                                                 sld, gate, stream);
+        hipError_t e = launch_index_select_fused(rd, q_idx, w, k_idx, bud.k_sink, bud.k_swa, ld, cols, bud.k_sparse,
+                                                 sk, sp, sld, gate, stream);
         if (e != hipSuccess)
             return e;
         return launch_topk_lists(rows->n_rows, n_seg, bud.k_sparse, ws, idx, gate, stream);

@@ -393,12 +393,12 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
     }
 }
 
-// SELECT (flat decode rows): instead of writing its scores, the block keeps them in LDS and writes its
-// chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
+// SELECT (flat decode rows): instead of writing its scores, the block keeps them in registers and writes
+// its chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
 // (sel_key / sel_pos [row][chunk * k_sel ..], key 0 / position -1 padded), so the fp32 scores never go
 // to HBM (their write traffic, interleaved with the key stream, slowed the stream by ~15 % at 1M).
-constexpr int kFusedV = kFusedCols / 256;                            // scores per thread (32)
-constexpr int kFusedLdsWords = kFusedCols + 2 * (kFusedCols / 32) + 16;  // keys by position, 2 bit maps, scan
+// LDS words of the fused epilogue for C-column chunks: keys by position, two bit maps, scan scratch.
+constexpr int fused_lds_words(int C) { return C + 2 * (C / 32) + 16; }
 
 // Epilogue of the fused scoring kernels, on scores held in registers: thread (wave w, lane (g, n)) holds
 // in s[j] the score of column (tile0 + 4 (4 j + w) + g) * 16 + n, i.e. of its j-th group of four tiles
@@ -408,12 +408,15 @@ constexpr int kFusedLdsWords = kFusedCols + 2 * (kFusedCols / 32) + 16;  // keys
 // columns (ties at the threshold in a second map, ranked by a scan over the map's words), and thread t
 // emits the picks of columns 32 t .. 32 t + 31.  The pairs (order key, position) go to chunk * k_sel
 // of row r's candidate list, padded with (0, -1).  lds: the block's idle ring, kFusedLdsWords words.
-__device__ inline void fused_select_regs(const float (&s)[kFusedV], uint32_t *lds, int64_t c_first, int64_t tile0,
+template <int C>
+__device__ inline void fused_select_regs(const float (&s)[C / 256], uint32_t *lds, int64_t c_first, int64_t tile0,
                                          int wave, int g, int n, int r, int64_t chunk, int k_sel,
                                          uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
                                          int64_t sel_ld)
 {
-    static_assert(kLdsWords + 16 <= kFusedLdsWords && kFusedCols / 32 == 256, "one bit-map word per thread");
+    constexpr int kFusedV = C / 256;   // scores per thread
+    constexpr int kMapW = C / 32 / 256;  // bit-map words per thread
+    static_assert(kLdsWords + 16 <= fused_lds_words(C) && kMapW >= 1 && C % (32 * 256) == 0, "whole map words");
     __syncthreads();  // every wave's ring DMA has landed: the ring's LDS is free
     uint32_t key[kFusedV];
 #pragma unroll
@@ -431,10 +434,11 @@ __device__ inline void fused_select_regs(const float (&s)[kFusedV], uint32_t *ld
         t_gt = sel.prefix << (32 - sel.consumed);
     else
         t_gt = sel.prefix + 1u, t_eq = sel.prefix;
-    uint32_t *pkey = lds, *gmap = lds + kFusedCols, *emap = gmap + kFusedCols / 32, *scan = emap + kFusedCols / 32;
+    uint32_t *pkey = lds, *gmap = lds + C, *emap = gmap + C / 32, *scan = emap + C / 32;
     __syncthreads();  // the selection's LDS is no longer read
-    gmap[threadIdx.x] = 0u;
-    emap[threadIdx.x] = 0u;
+#pragma unroll
+    for (int i = 0; i < kMapW; ++i)
+        gmap[kMapW * threadIdx.x + i] = emap[kMapW * threadIdx.x + i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m) {
@@ -446,23 +450,30 @@ __device__ inline void fused_select_regs(const float (&s)[kFusedV], uint32_t *ld
         }
     }
     __syncthreads();
-    const uint32_t gw = gmap[threadIdx.x], ew = emap[threadIdx.x];
+    uint32_t gw[kMapW], ew[kMapW], cg = 0, ce = 0;
+#pragma unroll
+    for (int i = 0; i < kMapW; ++i) {
+        gw[i] = gmap[kMapW * threadIdx.x + i], ew[i] = emap[kMapW * threadIdx.x + i];
+        cg += (uint32_t)__popc(gw[i]), ce += (uint32_t)__popc(ew[i]);
+    }
     uint32_t bg, be, tg, te;
-    block_scan2<256>((uint32_t)__popc(gw), (uint32_t)__popc(ew), bg, be, tg, te, scan);
+    block_scan2<256>(cg, ce, bg, be, tg, te, scan);
     uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
     int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
     uint32_t slot = bg + (be < sel.k_rem ? be : sel.k_rem);  // picks at lower positions
     uint32_t e_seen = be;
-    for (int b = 0; b < 32; ++b) {
-        const bool gb = (gw >> b) & 1u, eb = (ew >> b) & 1u;
-        if (gb || (eb && e_seen < sel.k_rem)) {
-            const uint32_t li = 32u * threadIdx.x + (uint32_t)b;
-            kout[slot] = pkey[li];
-            pout[slot] = (int32_t)(c_first + li);
-            ++slot;
+#pragma unroll
+    for (int i = 0; i < kMapW; ++i)
+        for (int b = 0; b < 32; ++b) {
+            const bool gb = (gw[i] >> b) & 1u, eb = (ew[i] >> b) & 1u;
+            if (gb || (eb && e_seen < sel.k_rem)) {
+                const uint32_t li = 32u * (kMapW * threadIdx.x + i) + (uint32_t)b;
+                kout[slot] = pkey[li];
+                pout[slot] = (int32_t)(c_first + li);
+                ++slot;
+            }
+            e_seen += eb ? 1u : 0u;
         }
-        e_seen += eb ? 1u : 0u;
-    }
     const uint32_t n_sel = tg + (te < sel.k_rem ? te : sel.k_rem);
     for (uint32_t i = n_sel + threadIdx.x; i < (uint32_t)k_sel; i += blockDim.x) {
         kout[i] = 0u;
@@ -470,7 +481,7 @@ __device__ inline void fused_select_regs(const float (&s)[kFusedV], uint32_t *ld
     }
 }
 
-template <int MODE, int S, bool SELECT>
+template <int MODE, int S, int SEL>
 __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ keys, int k_sink, int k_swa,
@@ -481,7 +492,9 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * kFusedLdsWords),
+    constexpr bool SELECT = SEL > 0;     // SEL: the fused pass's chunk width (0: write the scores)
+    constexpr int kFusedV = SELECT ? SEL / 256 : 1;
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * fused_lds_words(SEL)),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
@@ -518,9 +531,9 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
             out[c] = -INFINITY;
     }
     // SELECT: this lane's scores, one per group of four tiles (see fused_select_regs)
-    float sreg[SELECT ? kFusedV : 1];
+    float sreg[kFusedV];
 #pragma unroll
-    for (int m = 0; m < (SELECT ? kFusedV : 1); ++m)
+    for (int m = 0; m < kFusedV; ++m)
         sreg[m] = -INFINITY;
     int64_t sel_tile0 = 0;
     if (!empty) {  // (SELECT: a block without keys still publishes its empty candidate list below)
@@ -705,8 +718,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         }
     }
     if constexpr (SELECT)
-        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r, chunk,
-                          k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r,
+                               chunk, k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -762,15 +775,16 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
                                                          int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * kFusedLdsWords),
+    constexpr int kFusedV = SELECT ? kFusedCols / 256 : 1;
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * fused_lds_words(kFusedCols)),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
     stream_block<MODE>(r, chunk);
     __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
-    float sreg[SELECT ? kFusedV : 1];  // SELECT: this lane's scores, one per group of four tiles
+    float sreg[kFusedV];  // SELECT: this lane's scores, one per group of four tiles
 #pragma unroll
-    for (int m = 0; m < (SELECT ? kFusedV : 1); ++m)
+    for (int m = 0; m < kFusedV; ++m)
         sreg[m] = -INFINITY;
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
@@ -797,7 +811,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     } else if (empty) {  // no keys here: publish the empty candidate list
-        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
+        fused_select_regs<kFusedCols>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
                           sel_key, sel_pos, sel_ld);
         return;
     }
@@ -963,7 +977,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         wait_vmcnt<0>();
     }
     if constexpr (SELECT)
-        fused_select_regs(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
+        fused_select_regs<kFusedCols>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
                           k_sel, sel_key, sel_pos, sel_ld);
 }
 
@@ -1377,7 +1391,7 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
         } else {
             const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
-            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, false>), grid, dim3(256), 0, stream, rows,
+            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
                                ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
                                nullptr, 0);
@@ -1477,17 +1491,29 @@ bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int 
 
 int64_t index_select_fused_segments(int64_t n_cols) { return (n_cols + kFusedCols - 1) / kFusedCols; }
 
+// Chunk width of the bf16 fused pass: 16384 columns once that still gives two blocks per CU (half the
+// blocks, so half the per-block q loads, prologues and candidate lists), else 8192.
+int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols)
+{
+    return n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 512 ? 2 * kFusedCols : kFusedCols;
+}
+
 hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
-                                     int k_sink, int k_swa, int64_t n_cols, int k, uint32_t *sel_key,
+                                     int k_sink, int k_swa, int64_t n_cols, int64_t cols, int k, uint32_t *sel_key,
                                      int32_t *sel_pos, int64_t sel_ld, RowGate gate, hipStream_t stream)
 {
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
-    dim3 grid((unsigned)index_select_fused_segments(n_cols), (unsigned)rows.n_rows);
-    hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, true>), grid, dim3(256), 0, stream, rows,
-                       (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
-                       (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
-                       sel_ld);
+    dim3 grid((unsigned)((n_cols + cols - 1) / cols), (unsigned)rows.n_rows);
+    if (cols == 2 * kFusedCols)
+        hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
+                           rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1,
+                           nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld);
+    else
+        hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, kFusedCols>), grid, dim3(256), 0, stream, rows,
+                           (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
+                           (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
+                           sel_ld);
     return hipGetLastError();
 }
 

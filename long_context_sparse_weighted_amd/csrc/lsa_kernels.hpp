@@ -43,8 +43,9 @@ hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len
 // 64 rows: no 16-row groups); segments of index_select_fused_cols() columns
 bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int k);
 int64_t index_select_fused_segments(int64_t n_cols);
+int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols);  // bf16 chunk width: 8192 or 16384
 hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
-                                     int k_sink, int k_swa, int64_t n_cols, int k, uint32_t *sel_key,
+                                     int k_sink, int k_swa, int64_t n_cols, int64_t cols, int k, uint32_t *sel_key,
                                      int32_t *sel_pos, int64_t sel_ld, RowGate gate, hipStream_t stream);
 
 // --- FP8 indexer (index_score.hip): E4M3 codes, one power-of-two scale per vector

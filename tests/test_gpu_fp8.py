@@ -12,7 +12,7 @@ import synth
 from oracle import fp8
 from parity_util import (assert_idx_sets_match, assert_scores_close, budget_of, f64, host, kth_best, log, near_tie,
                          oracle_inputs, rows_of)
-from test_gpu_parity import FUSED_LENGTHS, FUSED_ROWS, RAGGED_LENGTHS, RAGGED_ROWS, custom_rows
+from test_gpu_parity import FUSED_LENGTHS, FUSED_ROWS, RAGGED_LENGTHS, RAGGED_ROWS, WIDE_FUSED_ROWS, custom_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -116,8 +116,7 @@ def test_fp8_selection_vs_oracle():
         assert set(picks) <= set(g_idx[b].tolist())
 
 
-# A larger fused batch than FUSED_ROWS: 42 rows x 25 segments of 8192 columns.
-FP8_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
+FP8_FUSED_ROWS = WIDE_FUSED_ROWS  # a larger fused batch: 42 rows x 25 segments of 8192 columns
 
 
 @pytest.mark.parametrize("k", [1, 1024, 4096])

@@ -465,6 +465,8 @@ def test_layer_bf16_decode_ragged():
 FUSED_LENGTHS = [1, 17, 1041, 1042, 3001, 8192, 8193, 20000, 40000, 200001]
 # (the last two rows sit at t = L_b: rows outside their sequence, which select nothing)
 FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9, 8192 + 1040), (6, 8193), (5, 8192)]
+# 42 rows x 13 chunks of 16384 columns: wide enough for the bf16 fused pass's 16384-column chunks
+WIDE_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
 
 
 @pytest.mark.parametrize("distinct", [1, 3, 40])
@@ -472,7 +474,7 @@ def test_index_topk_fused_ties(distinct):
     # keys drawn from a few distinct vectors, so every row's scores tie in long runs and the picks at the
     # threshold are decided by position (1: all candidates equal); the fused pass (14 rows x 25
     # segments) must match scoring then selecting bit for bit
-    x = custom_rows(FUSED_LENGTHS, FUSED_ROWS, attn=False, seed=46)
+    x = custom_rows(FUSED_LENGTHS, WIDE_FUSED_ROWS if distinct == 3 else FUSED_ROWS, attn=False, seed=46)
     n_tok = x["k_idx"].shape[0]
     pick = torch.randint(0, distinct, (n_tok,), generator=synth.generator(47, DEV), device=DEV)
     x["k_idx"] = x["k_idx"][:distinct].clone()[pick].contiguous()
@@ -502,7 +504,8 @@ def test_layer_fused_first_level_equals_separate_passes():
 def test_index_topk_equals_score_then_topk(k):
     # lsa_index_topk on the fused pass (14 rows x 25 segments of 8192 columns) and on the separate
     # passes (2 rows) against scoring everything and then selecting: bit-identical index sets
-    for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 42), ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
+    for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 42), (FUSED_LENGTHS, WIDE_FUSED_ROWS, 51),
+                                ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
         x = custom_rows(lengths, rows, attn=False, seed=seed)
         c = x["cfg"]
         bud = (c["k_sink"], c["k_swa"], k)

@@ -497,7 +497,7 @@ def main():
         "queries_per_s": round(args.batch / (head["latency_us"] * 1e-6), 1),
         "hbm_frac_layer": round(head["hbm_frac_layer"], 4),
         "mfma_frac_layer": round(head["flops"] / (head["latency_us"] * 1e-6) / BF16_PEAK, 4),
-        "roofline": {"kernel": "lsa_index_topk: score_stream_kernel<Flat, 5, select> (indexer scoring fused with "
+        "roofline": {"kernel": "lsa_index_topk: score_stream_kernel<Flat, 5, 16384> (indexer scoring fused with "
                                "the first top-K level) + topk_level_kernel over the candidate lists",
                      "bound": "hbm", "achieved": round(head["select_gbs"], 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                      "frac": round(head["select_gbs"] * 1e9 / HBM_PEAK, 4),

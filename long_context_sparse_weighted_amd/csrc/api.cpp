@@ -366,7 +366,8 @@ static size_t fp8_select_bytes(const lsa_rows_t *rows, int k, size_t *scores_byt
     const int64_t ld = rows->max_kv_len > 0 ? rows->max_kv_len : 1;
     if (fp8_fused(rows, k)) {
         *scores_bytes = 0;
-        return topk_lists_workspace_bytes(rows->n_rows, index_select_fused_segments(ld), k);
+        int64_t cols;
+        return topk_lists_workspace_bytes(rows->n_rows, flat_fused_segments(rows, ld, &cols), k);
     }
     *scores_bytes = align_up(sizeof(float) * (size_t)rows->n_rows * (size_t)ld);
     return *scores_bytes + topk_workspace_bytes(rows->n_rows, ld, k);
@@ -419,13 +420,14 @@ int lsa_index_topk_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q
     const int k = budget.k_sparse;
     hipError_t e;
     if (fp8_fused(rows, k)) {
-        const int64_t n_seg = index_select_fused_segments(ld);
+        int64_t cols;
+        const int64_t n_seg = flat_fused_segments(rows, ld, &cols);
         uint32_t *sk;
         int32_t *sp;
         int64_t sld;
         topk_first_lists(ws, rows->n_rows, n_seg, k, &sk, &sp, &sld);
-        e = launch_index_select_fused_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, ld, k, sk, sp,
-                                          sld, stream);
+        e = launch_index_select_fused_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, ld, cols, k, sk,
+                                          sp, sld, stream);
         if (e == hipSuccess)
             e = launch_topk_lists(rows->n_rows, n_seg, k, ws, idx, RowGate{nullptr, 0}, stream);
     } else {

@@ -746,6 +746,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 #define LSA_FP8_RING 4
 #endif
 constexpr int kFp8Ring = LSA_FP8_RING;
+constexpr int kFp8WideRing = 8;  // the 16384-column fused pass: its epilogue needs 68 KB of the ring
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kDim8 = 128;                          // bytes per key (E4M3 codes of d_I = 128)
 constexpr int kTileCodes8 = kTile * kDim8;          // 2 KB
@@ -764,7 +765,7 @@ __device__ inline void dma_4(const void *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
-template <int MODE, int S, bool SELECT>
+template <int MODE, int S, int SEL>
 __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
                                                          const float *__restrict__ q_scale,
                                                          const float *__restrict__ w, const uint8_t *__restrict__ k8,
@@ -775,8 +776,9 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
                                                          int32_t *__restrict__ sel_pos, int64_t sel_ld)
 {
     static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
-    constexpr int kFusedV = SELECT ? kFusedCols / 256 : 1;
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * fused_lds_words(kFusedCols)),
+    constexpr bool SELECT = SEL > 0;  // SEL: the fused pass's chunk width (0: write the scores)
+    constexpr int kFusedV = SELECT ? SEL / 256 : 1;
+    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * fused_lds_words(SEL)),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
@@ -811,7 +813,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     } else if (empty) {  // no keys here: publish the empty candidate list
-        fused_select_regs<kFusedCols>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
+        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
                           sel_key, sel_pos, sel_ld);
         return;
     }
@@ -977,18 +979,19 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         wait_vmcnt<0>();
     }
     if constexpr (SELECT)
-        fused_select_regs<kFusedCols>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
+        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
                           k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)
-#define LSA_FP8_INSTANCE(MODE, SEL)                                                                                 \
-    template __global__ void score_fp8_kernel<MODE, kFp8Ring, SEL>(                                                    \
+#define LSA_FP8_INSTANCE(MODE, RING, SEL)                                                                           \
+    template __global__ void score_fp8_kernel<MODE, RING, SEL>(                                                        \
         RowsDev, const uint8_t *, const float *, const float *, const uint8_t *, const float *, int, int,             \
         const int32_t *, int, int, float *, int64_t, int64_t, int64_t, int, uint32_t *, int32_t *, int64_t);
-LSA_FP8_INSTANCE(kModeFlat, false)
-LSA_FP8_INSTANCE(kModePaged, false)
-LSA_FP8_INSTANCE(kModeFlat, true)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, 0)
+LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, kFusedCols)
+LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols)
 #undef LSA_FP8_INSTANCE
 
 // ------------------------------------------------------------------------------------------
@@ -1444,11 +1447,11 @@ hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const 
     const ScoreGeom geo = score_geometry(rows.n_rows, ld, LSA_FP8_BLOCKS_PER_CU);
     dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
     if (pages)
-        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring, false>), grid, dim3(256), 0, stream, rows, q8,
+        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring, 0>), grid, dim3(256), 0, stream, rows, q8,
                            q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
                            nullptr, nullptr, (int64_t)0);
     else
-        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, false>), grid, dim3(256), 0, stream, rows, q8,
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, 0>), grid, dim3(256), 0, stream, rows, q8,
                            q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
                            nullptr, nullptr, (int64_t)0);
     return hipGetLastError();
@@ -1456,15 +1459,20 @@ hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const 
 
 hipError_t launch_index_select_fused_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,
                                          const uint8_t *k8, const float *k_scale, int k_sink, int k_swa,
-                                         int64_t n_cols, int k, uint32_t *sel_key, int32_t *sel_pos, int64_t sel_ld,
-                                         hipStream_t stream)
+                                         int64_t n_cols, int64_t cols, int k, uint32_t *sel_key, int32_t *sel_pos,
+                                         int64_t sel_ld, hipStream_t stream)
 {
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
-    dim3 grid((unsigned)index_select_fused_segments(n_cols), (unsigned)rows.n_rows);
-    hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, true>), grid, dim3(256), 0, stream, rows, q8, q_scale,
-                       w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols, (int64_t)kFusedCols,
-                       k, sel_key, sel_pos, sel_ld);
+    dim3 grid((unsigned)((n_cols + cols - 1) / cols), (unsigned)rows.n_rows);
+    if (cols == 2 * kFusedCols)
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8WideRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
+                           rows, q8, q_scale, w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols,
+                           cols, k, sel_key, sel_pos, sel_ld);
+    else
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, kFusedCols>), grid, dim3(256), 0, stream, rows, q8,
+                           q_scale, w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols,
+                           (int64_t)kFusedCols, k, sel_key, sel_pos, sel_ld);
     return hipGetLastError();
 }
 

@@ -57,8 +57,8 @@ hipError_t launch_quantize_fp8(int dtype, int64_t n_vec, int dim, const void *x,
 // FP8 scoring fused with the first top-K level (flat columns; segments as for the bf16 fused pass)
 hipError_t launch_index_select_fused_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,
                                          const uint8_t *k8, const float *k_scale, int k_sink, int k_swa,
-                                         int64_t n_cols, int k, uint32_t *sel_key, int32_t *sel_pos, int64_t sel_ld,
-                                         hipStream_t stream);
+                                         int64_t n_cols, int64_t cols, int k, uint32_t *sel_key, int32_t *sel_pos,
+                                         int64_t sel_ld, hipStream_t stream);
 
 // --- sub-block means (hi.hip)
 hipError_t launch_page_means(int dtype, int n_seq, const int64_t *kv_off, const int64_t *sb_off, const void *k_idx,

@@ -209,10 +209,6 @@ static hipError_t run_list_levels(int n_rows, int64_t n_in, int k, const TopkLis
         hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kFinalVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads),
                            0, stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,
                            gate.row_mode, gate.want);
-    else if (n_in <= 2 * kSegThreads * kFinalVpt)  // one row's list per block, so rows are few: twice the threads
-        hipLaunchKernelGGL((topk_level_kernel<2 * kSegThreads, kFinalVpt, false, true>), dim3(1, n_rows),
-                           dim3(2 * kSegThreads), 0, stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr,
-                           nullptr, 0, idx, gate.row_mode, gate.want);
     else
         hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0,
                            stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,

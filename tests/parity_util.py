@@ -86,8 +86,9 @@ def assert_attn_close(g_out, o_out, g_lse, o_lse, tol, what="attn"):
     assert err <= tol, f"{what}: max |out err| = {err:.3e} > {tol}"
     gl, ol = np.asarray(g_lse, np.float64), np.asarray(o_lse, np.float64)
     both_inf = np.isneginf(gl) & np.isneginf(ol)
-    lerr = np.abs(np.where(both_inf, 0.0, gl - ol))
-    ltol = 1e-4 * np.maximum(1.0, np.abs(np.where(both_inf, 0.0, ol)))
+    gl0, ol0 = np.where(both_inf, 0.0, gl), np.where(both_inf, 0.0, ol)  # (-inf on both sides agrees)
+    lerr = np.abs(gl0 - ol0)
+    ltol = 1e-4 * np.maximum(1.0, np.abs(ol0))
     worst = float((lerr / ltol).max()) if lerr.size else 0.0
     assert worst <= 1.0, f"{what}: lse err/tol = {worst:.3f}"
     return err

@@ -385,6 +385,24 @@ def bench_prefill(steps, warmup):
     return res
 
 
+def ragged_alg_bytes(lengths, drafts=3, hi_min_len=262144, P=128, B=128, M=1024, k_sink=16, k_swa=1024,
+                     k_sparse=1024):
+    """The method's own HBM bytes for one ragged MTP layer call: indexer keys of each flat owner row
+    (256 B per middle token), under HI the sub-block means of the causal pages and the keys of the M
+    recalled pages, the selected latent rows once per sequence (its drafts share them), and per row q,
+    out and lse (plus q_idx, w and idx per owner)."""
+    total = 0
+    for L in lengths:
+        mid = max(0, L - k_sink - k_swa)
+        if L >= hi_min_len:
+            total += (L + B - 1) // B * 256 + min(M * P, mid) * 256
+        else:
+            total += mid * 256
+        total += min(L, k_sink + k_swa + k_sparse) * 1152
+        total += drafts * (128 * 576 * 2 + 128 * 512 * 2 + 128 * 4) + 64 * 128 * 2 + 64 * 4 + k_sparse * 4
+    return total
+
+
 def bench_ragged(steps, warmup):
     """64 ragged sequences (4K-512K), 3 MTP drafts each sharing the first draft's index; HI for L >= 256K."""
     import torch
@@ -397,8 +415,11 @@ def bench_ragged(steps, warmup):
     km = lsa.lsa_page_means(x["kv_off"], sb_off, x["k_idx"], 128, x["max_len"])
     t, _ = time_layer(x, c, steps, warmup, idx_row=x["idx_row"], sb_off=sb_off, k_mean=km)
     n_hi = sum(1 for L in x["lengths"] if L >= 262144)
-    log(f"[bench] ragged MTP: {t * 1e6:.1f} us for 64 sequences (sum L = {sum(x['lengths'])}, {n_hi} on HI)")
-    return dict(latency_us=t * 1e6, sum_len=sum(x["lengths"]), hi_sequences=n_hi, queries_per_s=192 / t)
+    alg = ragged_alg_bytes(x["lengths"])
+    log(f"[bench] ragged MTP: {t * 1e6:.1f} us for 64 sequences (sum L = {sum(x['lengths'])}, {n_hi} on HI), "
+        f"{alg / 1e6:.1f} MB algorithmic = {alg / t / HBM_PEAK * 100:.1f}% of HBM peak")
+    return dict(latency_us=t * 1e6, sum_len=sum(x["lengths"]), hi_sequences=n_hi, queries_per_s=192 / t,
+                alg_bytes=alg, hbm_frac=alg / t / HBM_PEAK, hbm_bound_us=alg / HBM_PEAK * 1e6)
 
 
 def bench_tiny(steps, warmup):

@@ -115,6 +115,8 @@ int check_page_geometry(int dtype, int32_t P, int32_t B, int32_t M)
 // Workspace layout of lsa_layer_fwd.
 struct LayerWs {
     uint8_t *row_mode;
+    int32_t *row_lists;   // [2][n_rows]: flat rows, HI rows (ascending)
+    int32_t *row_counts;  // [2]
     void *topk_ws;
     float *page_scores;
     int32_t *pages;
@@ -129,7 +131,7 @@ struct LayerWs {
 // from 64K columns on; below that the separate passes, whose chunks shrink with the work, are faster).
 bool flat_fused(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k)
 {
-    return index_select_fusable(dtype, rows->n_rows, n_heads, head_dim, k) &&
+    return index_select_fusable(dtype, rows->n_rows, rows->n_seq, n_heads, head_dim, k) &&
            (int64_t)rows->n_rows * index_select_fused_segments(rows->max_kv_len) >= 256;
 }
 bool flat_fused(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows)
@@ -176,7 +178,8 @@ hipError_t launch_flat_select(int dtype, const lsa_rows_t *rows, const void *q_i
                                                  sk, sp, sld, gate, stream);
         if (e != hipSuccess)
             return e;
-        return launch_topk_lists(rows->n_rows, n_seg, bud.k_sparse, ws, idx, gate, stream);
+        return launch_topk_lists(rows->n_rows, n_seg, bud.k_sparse, ws, idx, gate,
+                                 ListCount{rd, bud.k_sink, bud.k_swa, cols, true}, stream);
     }
     size_t sb;
     (void)flat_select_bytes(dtype, rows, n_heads, head_dim, bud.k_sparse, &sb);
@@ -196,6 +199,8 @@ LayerWs layer_ws_layout(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, bool
     const int k_total = cfg->budget.k_sink + cfg->budget.k_swa + cfg->budget.k_sparse;
     if (cfg->is_owner) {
         w.row_mode = (uint8_t *)c.take((size_t)n);
+        w.row_lists = (int32_t *)c.take(sizeof(int32_t) * 2 * (size_t)n);
+        w.row_counts = (int32_t *)c.take(sizeof(int32_t) * 2);
         // The flat and the HI token top-K share one workspace.  Rows scored one by one take the fused
         // scoring + first top-K level, which writes candidate lists instead of scores.
         size_t sb;
@@ -429,7 +434,8 @@ int lsa_index_topk_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q
         e = launch_index_select_fused_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, ld, cols, k, sk,
                                           sp, sld, stream);
         if (e == hipSuccess)
-            e = launch_topk_lists(rows->n_rows, n_seg, k, ws, idx, RowGate{nullptr, 0}, stream);
+            e = launch_topk_lists(rows->n_rows, n_seg, k, ws, idx, RowGate{nullptr, 0},
+                                  ListCount{rd, budget.k_sink, budget.k_swa, cols, true}, stream);
     } else {
         float *scores = (float *)ws;
         e = launch_index_score_fp8(rd, q8, q_scale, w, k8, k_scale, budget.k_sink, budget.k_swa, nullptr, 0, 1, scores,
@@ -729,12 +735,15 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
         const bool all_hi = use_hi && rows->min_kv_len >= cfg->hi_min_len;
         const bool need_modes = (use_hi && !all_hi) || idx_row != nullptr;
         if (need_modes)
-            e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, stream);
+            e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, lw.row_lists,
+                                 lw.row_counts, stream);
         const uint8_t *gate = need_modes ? lw.row_mode : nullptr;
+        const int32_t *flat_list = need_modes ? lw.row_lists : nullptr;
+        const int32_t *hi_list = need_modes ? lw.row_lists + rows->n_rows : nullptr;
         // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
         if (e == hipSuccess && !all_hi)
             e = launch_flat_select(cfg->dtype, rows, q_idx, w, k_idx, cfg->n_heads_idx, cfg->head_dim_idx, bud, idx,
-                                   lw.topk_ws, RowGate{gate, 1}, stream);
+                                   lw.topk_ws, RowGate{gate, 1, flat_list, lw.row_counts}, stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);
@@ -749,7 +758,7 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
             if (e == hipSuccess)
                 e = launch_index_score(cfg->dtype, rd, rows->max_kv_len, q_idx, w, k_idx, cfg->n_heads_idx,
                                        cfg->head_dim_idx, bud.k_sink, bud.k_swa, lw.pages, cfg->M, cfg->P,
-                                       lw.comp_scores, n_comp, RowGate{gate, 2}, stream);
+                                       lw.comp_scores, n_comp, RowGate{gate, 2, hi_list, lw.row_counts + 1}, stream);
             if (e == hipSuccess)
                 e = launch_topk(rows->n_rows, lw.comp_scores, n_comp, n_comp, lw.pages, cfg->M, cfg->P, bud.k_sparse,
                                 idx, lw.topk_ws, RowGate{gate, 2}, stream);

@@ -828,16 +828,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int n_heads, int n_spli
 
 constexpr int kMaxSplit = kMaxSplitMerge;
 
+// Splits of each row's selected list: the grid runs in rounds of 256 blocks (one per CU), a block costs
+// its tiles plus a fixed part (Q load, pick compaction, partial store: about 5 tiles' worth), so the
+// split count minimises rounds x (tiles per split + 5), with at least 4 tiles per split.
 static int pick_split(int n_rows, int n_heads, int k_total)
 {
-    int blocks_per_split = n_rows * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
-    int want = (256 + blocks_per_split - 1) / blocks_per_split;  // about one block per CU
-    int max_by_tiles = (k_total + kRowsPerTile - 1) / kRowsPerTile / 4;  // >= 4 tiles per split
-    if (want > max_by_tiles)
-        want = max_by_tiles;
-    if (want > kMaxSplit)
-        want = kMaxSplit;
-    return want < 1 ? 1 : want;
+    const int64_t row_blocks = (int64_t)n_rows * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+    const int n_tiles = (k_total + kRowsPerTile - 1) / kRowsPerTile;
+    const int max_split = min(kMaxSplit, max(1, n_tiles / 4));
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    for (int ns = 1; ns <= max_split; ++ns) {
+        const int64_t rounds = (row_blocks * ns + 255) / 256;
+        const int64_t cost = rounds * ((n_tiles + ns - 1) / ns + 5);
+        if (cost < best_cost) {
+            best_cost = cost;
+            best = ns;
+        }
+    }
+    return best;
 }
 
 size_t attn_workspace_bytes(int dtype, int n_rows, int n_heads, int d_v, int k_total)

@@ -338,21 +338,37 @@ constexpr int kFusedCols = 8192;
 constexpr int kFusedRing = 5;
 
 // Block -> (row, chunk) of the streaming kernels.  Blocks go to the 8 XCDs in turn, in launch order
-// (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  A paged row's chunks can
+// (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  The fused selection passes
+// (SELECT) are taken chunk by chunk as the paged ones below: in a ragged batch the chunks past a short
+// row's range exit at once, and the chunk-major order puts the busy low chunks of all rows first.  A paged row's chunks can
 // differ a lot in work (a recall list that is mostly padding leaves its last chunks empty), so paged
 // blocks are taken chunk by chunk instead, all rows of a chunk before the next chunk, with the rows
 // rotated by the chunk index: the busy first chunks come first and are spread over every XCD, and
 // the chunks of one row still land on different XCDs.
-template <int MODE>
+template <int MODE, bool CHUNK_MAJOR = MODE == kModePaged>
 __device__ inline void stream_block(int &r, int64_t &chunk)
 {
     r = blockIdx.y;
     chunk = blockIdx.x;
-    if constexpr (MODE == kModePaged) {
+    if constexpr (CHUNK_MAJOR) {
         const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
         chunk = lin / gridDim.y;
         r = (int)((lin % gridDim.y + chunk) % gridDim.y);
     }
+}
+
+// With a compact list of the wanted rows (count on the device) the blocks are taken in that list's order,
+// chunk by chunk: block i of the (chunks x n_rows) grid is chunk i / count of list row i % count, so every
+// block that has work comes before every block that has none.  Returns false for a block without work.
+__device__ inline bool stream_block_listed(const int32_t *row_list, const int32_t *row_count, int &r, int64_t &chunk)
+{
+    const int64_t cnt = *row_count;
+    const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    if (lin >= cnt * (int64_t)gridDim.x)
+        return false;
+    chunk = lin / cnt;
+    r = row_list[lin % cnt];
+    return true;
 }
 
 // Columns of the chunk [c_first, c_last) that can hold keys: [c_begin, c_end) (empty when
@@ -489,7 +505,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             float *__restrict__ scores, int64_t ld, int64_t n_cols,
                                                             int64_t cols_per_block, const uint8_t *row_mode, int want,
                                                             int grouped, int k_sel, uint32_t *__restrict__ sel_key,
-                                                            int32_t *__restrict__ sel_pos, int64_t sel_ld)
+                                                            int32_t *__restrict__ sel_pos, int64_t sel_ld,
+                                                            const int32_t *row_list, const int32_t *row_count)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
     constexpr bool SELECT = SEL > 0;     // SEL: the fused pass's chunk width (0: write the scores)
@@ -498,11 +515,16 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
-    stream_block<MODE>(r, chunk);
-    if (row_mode && row_mode[r] != want)
-        return;
-    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
-        return;  // scored by the multi-row kernel
+    if (row_list) {
+        if (!stream_block_listed(row_list, row_count, r, chunk))
+            return;
+    } else {
+        stream_block<MODE, MODE == kModePaged || SELECT>(r, chunk);
+        if (row_mode && row_mode[r] != want)
+            return;
+        if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
+            return;  // scored by the multi-row kernel
+    }
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
@@ -513,6 +535,12 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
     const int g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar tile math
     const int64_t c_first = chunk * cols_per_block;
+    if constexpr (SELECT) {
+        // chunks past the row's scored range publish no list (fused_row_lists: the later levels read
+        // only the lists of the chunks before it), so a short row of a ragged batch costs nothing here
+        if (cm.lo >= cm.hi || c_first >= cm.hi)
+            return;
+    }
     const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
     float *out = scores + (int64_t)r * ld;
     // Columns of this chunk that can hold keys: [c_begin, c_end); the others are written -inf.
@@ -782,7 +810,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
-    stream_block<MODE>(r, chunk);
+    stream_block<MODE, MODE == kModePaged || SELECT>(r, chunk);
     __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
     float sreg[kFusedV];  // SELECT: this lane's scores, one per group of four tiles
 #pragma unroll
@@ -797,6 +825,10 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
     const int g = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t c_first = chunk * cols_per_block;
+    if constexpr (SELECT) {
+        if (cm.lo >= cm.hi || c_first >= cm.hi)
+            return;  // past the row's scored range: no list (see fused_row_lists)
+    }
     const int64_t c_last = c_first + cols_per_block < n_cols ? c_first + cols_per_block : n_cols;
     float *out = scores + (int64_t)r * ld;
     int64_t c_begin, c_end;
@@ -1392,12 +1424,18 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
                                (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
                                geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
         } else {
-            const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
+            ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
+            if (MODE == kModePaged && (rows.n_rows < kMinGroupedRows || rows.n_rows < kGroupRows * rows.n_seq) &&
+                sgeo.chunk_elems > 2048) {
+                // decode-like rows, of which only some (those at least hi_min_len long) may run HI: chunks
+                // of 2048 columns (16 pages of 128) keep a few HI rows spread over the whole chip
+                sgeo = ScoreGeom{2048, (int)((n_cols + 2047) / 2048)};
+            }
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
             hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
                                ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
-                               nullptr, 0);
+                               nullptr, 0, grouped ? nullptr : gate.list, gate.count);
         }
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
@@ -1491,10 +1529,12 @@ hipError_t launch_quantize_fp8(int dtype, int64_t n_vec, int dim, const void *x,
     return hipGetLastError();
 }
 
-bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int k)
+// Rows are scored one by one (and so can take the fused pass) unless they are prefill-like: many rows
+// per sequence, which the 16-row grouped kernel scores from shared key stages.
+bool index_select_fusable(int dtype, int n_rows, int n_seq, int n_heads, int head_dim, int k)
 {
-    return dtype == 1 && n_heads == kHeads && head_dim == kDim && n_rows < kMinGroupedRows && k >= 1 &&
-           k <= kMaxLocalK;
+    const bool per_row = n_rows < kMinGroupedRows || (int64_t)n_rows < (int64_t)kGroupRows * n_seq;
+    return dtype == 1 && n_heads == kHeads && head_dim == kDim && per_row && k >= 1 && k <= kMaxLocalK;
 }
 
 int64_t index_select_fused_segments(int64_t n_cols) { return (n_cols + kFusedCols - 1) / kFusedCols; }
@@ -1503,7 +1543,11 @@ int64_t index_select_fused_segments(int64_t n_cols) { return (n_cols + kFusedCol
 // blocks, so half the per-block q loads, prologues and candidate lists), else 8192.
 int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols)
 {
-    return n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 512 ? 2 * kFusedCols : kFusedCols;
+    // (a batch of more than 64 rows is taken to be ragged: the chunks of its short rows are empty, so
+    // n_rows x chunks overstates the work, and the narrower chunks keep two blocks per CU)
+    return n_rows < kMinGroupedRows && n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 512
+               ? 2 * kFusedCols
+               : kFusedCols;
 }
 
 hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
@@ -1516,12 +1560,13 @@ hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, con
     if (cols == 2 * kFusedCols)
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
                            rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1,
-                           nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld);
+                           nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld,
+                           gate.list, gate.count);
     else
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, kFusedCols>), grid, dim3(256), 0, stream, rows,
                            (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
                            (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
-                           sel_ld);
+                           sel_ld, gate.list, gate.count);
     return hipGetLastError();
 }
 

@@ -6,33 +6,65 @@
 // [paper] §3.3 "Design choices", §4.1.2).  Decided on the device from kv_off, so the host never
 // reads sequence lengths.
 #include "lsa_kernels.hpp"
+#include "topk_block.hpp"
 
 namespace lsa {
 
-__global__ void row_modes_kernel(RowsDev rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
-                                 uint8_t *row_mode)
+// One block of 1024 threads: thread t decides the modes of rows [t per, t per + per) and the block scan
+// of the per-thread counts places the flat and HI rows in their lists in ascending row order.
+constexpr int kModeThreads = 1024;
+
+__global__ __launch_bounds__(kModeThreads) void row_modes_kernel(RowsDev rows, const int32_t *idx_row,
+                                                                 int64_t hi_min_len, int hi_enabled,
+                                                                 uint8_t *row_mode, int32_t *lists, int32_t *counts)
 {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= rows.n_rows)
-        return;
-    uint8_t mode = 1;
-    if (idx_row && idx_row[r] != r) {
-        mode = 0;
-    } else if (hi_enabled) {
-        int32_t b = rows.row_seq[r];
-        if (b >= 0 && b < rows.n_seq && rows.kv_off[b + 1] - rows.kv_off[b] >= hi_min_len)
-            mode = 2;
+    __shared__ uint32_t scan[2 * kModeThreads / kWave];
+    const int n = rows.n_rows;
+    const int per = (n + kModeThreads - 1) / kModeThreads;
+    const int r0 = threadIdx.x * per;
+    auto mode_of = [&](int r) -> uint8_t {
+        if (idx_row && idx_row[r] != r)
+            return 0;
+        if (hi_enabled) {
+            const int32_t b = rows.row_seq[r];
+            if (b >= 0 && b < rows.n_seq && rows.kv_off[b + 1] - rows.kv_off[b] >= hi_min_len)
+                return 2;
+        }
+        return 1;
+    };
+    uint32_t c1 = 0, c2 = 0;
+    for (int i = 0; i < per; ++i) {
+        const int r = r0 + i;
+        if (r < n) {
+            const uint8_t m = mode_of(r);
+            row_mode[r] = m;
+            c1 += m == 1 ? 1u : 0u;
+            c2 += m == 2 ? 1u : 0u;
+        }
     }
-    row_mode[r] = mode;
+    uint32_t e1, e2, t1, t2;
+    block_scan2<kModeThreads>(c1, c2, e1, e2, t1, t2, scan);
+    for (int i = 0; i < per; ++i) {
+        const int r = r0 + i;
+        if (r < n) {
+            const uint8_t m = row_mode[r];  // (this thread's own write)
+            if (m == 1)
+                lists[e1++] = r;
+            else if (m == 2)
+                lists[n + e2++] = r;
+        }
+    }
+    if (threadIdx.x == 0)
+        counts[0] = (int32_t)t1, counts[1] = (int32_t)t2;
 }
 
 hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
-                            uint8_t *row_mode, hipStream_t stream)
+                            uint8_t *row_mode, int32_t *lists, int32_t *counts, hipStream_t stream)
 {
     if (rows.n_rows == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(row_modes_kernel, dim3((rows.n_rows + 255) / 256), dim3(256), 0, stream, rows, idx_row,
-                       hi_min_len, hi_enabled, row_mode);
+    hipLaunchKernelGGL(row_modes_kernel, dim3(1), dim3(kModeThreads), 0, stream, rows, idx_row, hi_min_len,
+                       hi_enabled, row_mode, lists, counts);
     return hipGetLastError();
 }
 

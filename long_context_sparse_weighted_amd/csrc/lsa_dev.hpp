@@ -79,6 +79,17 @@ __device__ inline SiRanges si_ranges(const RowInfo &ri, int k_sink, int k_swa)
     return g;
 }
 
+// Candidate lists of row r after a fused scoring + first top-K pass on chunks of C columns: one list per
+// chunk from column 0 to the end of the row's scored range min(mid_hi, L), none when that range is
+// empty.  Chunks past it write nothing, and the later top-K levels read only these lists.
+__device__ inline int64_t fused_row_lists(const RowsDev &rows, int r, int k_sink, int k_swa, int64_t C)
+{
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges g = si_ranges(ri, k_sink, k_swa);
+    const int64_t hi = g.mid_hi < ri.L ? g.mid_hi : ri.L;
+    return hi > g.mid_lo ? (hi + C - 1) / C : 0;
+}
+
 // ------------------------------------------------------------------------------- bf16 / floats
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -10,9 +10,22 @@
 namespace lsa {
 
 // Row gating for the layer: when row_mode != nullptr, only rows with row_mode[r] == want run.
+// list / count (optional, streaming scoring kernels only): the rows with row_mode[r] == want in ascending
+// order and their number, so that the blocks of those rows can be launched first.
 struct RowGate {
     const uint8_t *row_mode;
     int want;
+    const int32_t *list = nullptr;
+    const int32_t *count = nullptr;
+};
+
+// Per-row input sizes of the candidate-list levels after a fused first level (on = false: every row has
+// the uniform count): row r starts with fused_row_lists(rows, r, k_sink, k_swa, cols) lists of k.
+struct ListCount {
+    RowsDev rows;
+    int k_sink, k_swa;
+    int64_t cols;
+    bool on;
 };
 
 // --- top-k (topk.hip): exact selection of the k best (score desc, position asc), 1 <= k <= 4096.
@@ -20,7 +33,8 @@ struct RowGate {
 // buffers to fill, and the remaining levels down to idx.
 size_t topk_lists_workspace_bytes(int n_rows, int64_t n_seg, int k);
 void topk_first_lists(void *ws, int n_rows, int64_t n_seg, int k, uint32_t **key, int32_t **pos, int64_t *ld);
-hipError_t launch_topk_lists(int n_rows, int64_t n_seg, int k, void *ws, int32_t *idx, RowGate gate, hipStream_t stream);
+hipError_t launch_topk_lists(int n_rows, int64_t n_seg, int k, void *ws, int32_t *idx, RowGate gate, ListCount cnt,
+                             hipStream_t stream);
 size_t topk_workspace_bytes(int n_rows, int64_t n_cols, int k);
 hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_cols, const int32_t *pages, int M,
                        int P, int k, int32_t *idx, void *ws, RowGate gate, hipStream_t stream);
@@ -41,7 +55,7 @@ hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len
 
 // --- fused flat scoring + first top-K level (index_score.hip), for rows scored one by one (fewer than
 // 64 rows: no 16-row groups); segments of index_select_fused_cols() columns
-bool index_select_fusable(int dtype, int n_rows, int n_heads, int head_dim, int k);
+bool index_select_fusable(int dtype, int n_rows, int n_seq, int n_heads, int head_dim, int k);
 int64_t index_select_fused_segments(int64_t n_cols);
 int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols);  // bf16 chunk width: 8192 or 16384
 hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, const float *w, const void *k_idx,
@@ -73,8 +87,10 @@ hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, con
                               const int32_t *idx_row, void *out, float *lse, void *ws, hipStream_t stream);
 
 // --- layer helpers (layer.hip)
+// Also writes, for modes 1 and 2, the rows of that mode in ascending order (lists [2][n_rows]) and their
+// numbers (counts[2]).
 hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
-                            uint8_t *row_mode, hipStream_t stream);
+                            uint8_t *row_mode, int32_t *lists, int32_t *counts, hipStream_t stream);
 
 // Rounds a byte count up to the workspace alignment.
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -31,6 +31,7 @@ constexpr int kVpt = kSeg / kSegThreads;        // keys per thread
 constexpr int kSmallThreads = 256;
 constexpr int kSmallVpt = 16;                   // a row of at most 4096 columns: one block of 256 x 16
 constexpr int kFinalVpt = 16;                   // a final candidate list of at most 8192: 512 x 16
+constexpr int64_t kListSeg = kSeg;              // candidates per segment of the non-final list levels
 
 
 // One level.  SRC_SCORES: segment `seg` of row r is columns [seg * 64 NT, ...) of the scores (page
@@ -45,11 +46,23 @@ __global__ __launch_bounds__(NT) void topk_level_kernel(const float *__restrict_
                                                          const int32_t *__restrict__ in_pos, int64_t in_ld, int k,
                                                          uint32_t *__restrict__ out_key, int32_t *__restrict__ out_pos,
                                                          int64_t out_ld, int32_t *__restrict__ idx,
-                                                         const uint8_t *row_mode, int want)
+                                                         const uint8_t *row_mode, int want, ListCount cnt,
+                                                         int level)
 {
     const int seg = blockIdx.x, r = blockIdx.y;
     if (row_mode && row_mode[r] != want)
         return;
+    if constexpr (!SRC_SCORES) {
+        if (cnt.on) {
+            // this row's own list length at this level (its first level wrote fused_row_lists lists)
+            int64_t m = fused_row_lists(cnt.rows, r, cnt.k_sink, cnt.k_swa, cnt.cols) * k;
+            for (int l = 0; l < level; ++l)
+                m = (m + kListSeg - 1) / kListSeg * k;  // each level keeps k per segment of kListSeg
+            n_in = m < n_in ? m : n_in;
+            if (!FINAL && (int64_t)seg * (VPT * NT) >= n_in)
+                return;  // past the row's lists: nothing to read and nothing the next level reads
+        }
+    }
     // LDS: the histograms, reused afterwards as the staging area of the picks.
     __shared__ __attribute__((aligned(16))) uint32_t lds[kLdsWords];
     __shared__ uint32_t scratch[3 * NT / kWave];
@@ -189,18 +202,21 @@ static TopkLists topk_lists(void *ws, int n_rows, int64_t l0, int64_t l1)
 // The levels after the first: lists of n_in candidates per row in t's A buffers, reduced segment by
 // segment until one remains, whose picks go to idx.
 static hipError_t run_list_levels(int n_rows, int64_t n_in, int k, const TopkLists &t, int32_t *idx, RowGate gate,
-                                  hipStream_t stream)
+                                  ListCount cnt, hipStream_t stream)
 {
     bool in_a = true;
+    int level = 0;
     while (n_in > kSeg) {  // reduce the candidate lists further
         const int64_t segs = (n_in + kSeg - 1) / kSeg;
         const int64_t n_out = segs * k;
         hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, false>), dim3((unsigned)segs, n_rows),
                            dim3(kSegThreads), 0, stream, nullptr, 0, n_in, nullptr, 0, 1, in_a ? t.key_a : t.key_b,
                            in_a ? t.pos_a : t.pos_b, in_a ? t.lda : t.ldb, k, in_a ? t.key_b : t.key_a,
-                           in_a ? t.pos_b : t.pos_a, in_a ? t.ldb : t.lda, nullptr, gate.row_mode, gate.want);
+                           in_a ? t.pos_b : t.pos_a, in_a ? t.ldb : t.lda, nullptr, gate.row_mode, gate.want, cnt,
+                           level);
         n_in = n_out;
         in_a = !in_a;
+        ++level;
     }
     const uint32_t *fk = in_a ? t.key_a : t.key_b;
     const int32_t *fp = in_a ? t.pos_a : t.pos_b;
@@ -208,11 +224,11 @@ static hipError_t run_list_levels(int n_rows, int64_t n_in, int k, const TopkLis
     if (n_in <= kSegThreads * kFinalVpt)  // (8 segments' picks at 128K columns): half the keys per thread
         hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kFinalVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads),
                            0, stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,
-                           gate.row_mode, gate.want);
+                           gate.row_mode, gate.want, cnt, level);
     else
         hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, false, true>), dim3(1, n_rows), dim3(kSegThreads), 0,
                            stream, nullptr, 0, n_in, nullptr, 0, 1, fk, fp, fld, k, nullptr, nullptr, 0, idx,
-                           gate.row_mode, gate.want);
+                           gate.row_mode, gate.want, cnt, level);
     return hipGetLastError();
 }
 
@@ -242,18 +258,18 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
         if (n_cols <= kSmallVpt * kSmallThreads)
             hipLaunchKernelGGL((topk_level_kernel<kSmallThreads, kSmallVpt, true, true>), dim3(1, n_rows),
                                dim3(kSmallThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
-                               nullptr, nullptr, 0, idx, gate.row_mode, gate.want);
+                               nullptr, nullptr, 0, idx, gate.row_mode, gate.want, ListCount{}, 0);
         else
             hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, true>), dim3(1, n_rows), dim3(kSegThreads),
                                0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, nullptr, nullptr, 0,
-                               idx, gate.row_mode, gate.want);
+                               idx, gate.row_mode, gate.want, ListCount{}, 0);
         return hipGetLastError();
     }
     TopkLists t = topk_lists(ws, n_rows, l0, l1);
     hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, false>), dim3((unsigned)n_seg, n_rows),
                        dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, t.key_a,
-                       t.pos_a, t.lda, nullptr, gate.row_mode, gate.want);
-    return run_list_levels(n_rows, l0, k, t, idx, gate, stream);
+                       t.pos_a, t.lda, nullptr, gate.row_mode, gate.want, ListCount{}, 0);
+    return run_list_levels(n_rows, l0, k, t, idx, gate, ListCount{}, stream);
 }
 
 size_t topk_lists_workspace_bytes(int n_rows, int64_t n_seg, int k)
@@ -271,14 +287,15 @@ void topk_first_lists(void *ws, int n_rows, int64_t n_seg, int k, uint32_t **key
     *ld = t.lda;
 }
 
-hipError_t launch_topk_lists(int n_rows, int64_t n_seg, int k, void *ws, int32_t *idx, RowGate gate, hipStream_t stream)
+hipError_t launch_topk_lists(int n_rows, int64_t n_seg, int k, void *ws, int32_t *idx, RowGate gate, ListCount cnt,
+                             hipStream_t stream)
 {
     if (k < 1 || k > kMaxLocalK)
         return hipErrorInvalidValue;
     if (n_rows == 0)
         return hipSuccess;
     const int64_t l0 = n_seg * k, l1 = ((l0 + kSeg - 1) / kSeg) * k;
-    return run_list_levels(n_rows, l0, k, topk_lists(ws, n_rows, l0, l1), idx, gate, stream);
+    return run_list_levels(n_rows, l0, k, topk_lists(ws, n_rows, l0, l1), idx, gate, cnt, stream);
 }
 
 }  // namespace lsa

@@ -116,7 +116,10 @@ int check_page_geometry(int dtype, int32_t P, int32_t B, int32_t M)
 struct LayerWs {
     uint8_t *row_mode;
     int32_t *row_lists;   // [2][n_rows]: flat rows, HI rows (ascending)
-    int32_t *row_counts;  // [2]
+    int32_t *row_counts;  // [3]: flat rows, HI rows, fused-pass blocks with work
+    int32_t *fused_table; // [2 * fused_cap]: (row, chunk) of those blocks
+    int64_t fused_cap;
+    int64_t fused_cols;   // chunk width of the fused flat pass (0: not fused)
     void *topk_ws;
     float *page_scores;
     int32_t *pages;
@@ -200,7 +203,14 @@ LayerWs layer_ws_layout(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, bool
     if (cfg->is_owner) {
         w.row_mode = (uint8_t *)c.take((size_t)n);
         w.row_lists = (int32_t *)c.take(sizeof(int32_t) * 2 * (size_t)n);
-        w.row_counts = (int32_t *)c.take(sizeof(int32_t) * 2);
+        w.row_counts = (int32_t *)c.take(sizeof(int32_t) * 4);
+        w.fused_cols = 0;
+        w.fused_cap = 0;
+        if (flat_fused(cfg, rows)) {
+            const int64_t segs = flat_fused_segments(rows, rows->max_kv_len > 0 ? rows->max_kv_len : 1, &w.fused_cols);
+            w.fused_cap = segs * n;
+        }
+        w.fused_table = (int32_t *)c.take(sizeof(int32_t) * 2 * (size_t)w.fused_cap);
         // The flat and the HI token top-K share one workspace.  Rows scored one by one take the fused
         // scoring + first top-K level, which writes candidate lists instead of scores.
         size_t sb;
@@ -736,14 +746,18 @@ int lsa_layer_fwd(const lsa_layer_cfg_t *cfg, const lsa_rows_t *rows, const int3
         const bool need_modes = (use_hi && !all_hi) || idx_row != nullptr;
         if (need_modes)
             e = launch_row_modes(rd, idx_row, cfg->hi_min_len, use_hi ? 1 : 0, lw.row_mode, lw.row_lists,
-                                 lw.row_counts, stream);
+                                 lw.row_counts, bud.k_sink, bud.k_swa, lw.fused_cols, lw.fused_table, lw.fused_cap,
+                                 stream);
         const uint8_t *gate = need_modes ? lw.row_mode : nullptr;
         const int32_t *flat_list = need_modes ? lw.row_lists : nullptr;
         const int32_t *hi_list = need_modes ? lw.row_lists + rows->n_rows : nullptr;
         // Flat indexer rows ([paper] §2.2 Eq. 1-2 over mid(t)).
         if (e == hipSuccess && !all_hi)
             e = launch_flat_select(cfg->dtype, rows, q_idx, w, k_idx, cfg->n_heads_idx, cfg->head_dim_idx, bud, idx,
-                                   lw.topk_ws, RowGate{gate, 1, flat_list, lw.row_counts}, stream);
+                                   lw.topk_ws,
+                                   RowGate{gate, 1, flat_list, lw.row_counts, need_modes ? lw.fused_table : nullptr,
+                                           lw.row_counts + 2},
+                                   stream);
         if (use_hi) {
             // HI rows ([paper] §3.3): page recall, stage-2 scoring on the recalled pages, topK.
             const int64_t n_pages = ceil_div(rows->max_kv_len, cfg->P);

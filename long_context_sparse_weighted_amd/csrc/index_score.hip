@@ -506,7 +506,8 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                                                             int64_t cols_per_block, const uint8_t *row_mode, int want,
                                                             int grouped, int k_sel, uint32_t *__restrict__ sel_key,
                                                             int32_t *__restrict__ sel_pos, int64_t sel_ld,
-                                                            const int32_t *row_list, const int32_t *row_count)
+                                                            const int32_t *row_list, const int32_t *row_count,
+                                                            const int32_t *blk_table, const int32_t *blk_count)
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
     constexpr bool SELECT = SEL > 0;     // SEL: the fused pass's chunk width (0: write the scores)
@@ -515,7 +516,16 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
-    if (row_list) {
+    if (blk_table) {
+        // the blocks with work, (row, chunk) in order: block i takes entry i, the rest have none
+        const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        if (lin >= *blk_count)
+            return;
+        r = blk_table[2 * lin];
+        chunk = blk_table[2 * lin + 1];
+        if (chunk >= (int64_t)gridDim.x)
+            return;  // (a row longer than max_kv_len: its lists would not fit the candidate buffers)
+    } else if (row_list) {
         if (!stream_block_listed(row_list, row_count, r, chunk))
             return;
     } else {
@@ -1435,7 +1445,7 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
             hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
                                (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
                                ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
-                               nullptr, 0, grouped ? nullptr : gate.list, gate.count);
+                               nullptr, 0, grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
         }
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
@@ -1561,12 +1571,12 @@ hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, con
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
                            rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1,
                            nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld,
-                           gate.list, gate.count);
+                           gate.list, gate.count, gate.table, gate.table_count);
     else
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, kFusedCols>), grid, dim3(256), 0, stream, rows,
                            (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
                            (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
-                           sel_ld, gate.list, gate.count);
+                           sel_ld, gate.list, gate.count, gate.table, gate.table_count);
     return hipGetLastError();
 }
 

@@ -16,7 +16,9 @@ constexpr int kModeThreads = 1024;
 
 __global__ __launch_bounds__(kModeThreads) void row_modes_kernel(RowsDev rows, const int32_t *idx_row,
                                                                  int64_t hi_min_len, int hi_enabled,
-                                                                 uint8_t *row_mode, int32_t *lists, int32_t *counts)
+                                                                 uint8_t *row_mode, int32_t *lists, int32_t *counts,
+                                                                 int k_sink, int k_swa, int64_t fused_cols,
+                                                                 int32_t *table, int64_t table_cap)
 {
     __shared__ uint32_t scan[2 * kModeThreads / kWave];
     const int n = rows.n_rows;
@@ -56,15 +58,39 @@ __global__ __launch_bounds__(kModeThreads) void row_modes_kernel(RowsDev rows, c
     }
     if (threadIdx.x == 0)
         counts[0] = (int32_t)t1, counts[1] = (int32_t)t2;
+    if (fused_cols <= 0)
+        return;
+    // The fused pass's blocks with work: fused_row_lists(r) chunks of each flat row, in row order.
+    uint32_t nb = 0;
+    for (int i = 0; i < per; ++i) {
+        const int r = r0 + i;
+        if (r < n && row_mode[r] == 1)
+            nb += (uint32_t)fused_row_lists(rows, r, k_sink, k_swa, fused_cols);
+    }
+    uint32_t eb, e0, tb, t0;
+    __syncthreads();  // (scan scratch reuse)
+    block_scan2<kModeThreads>(nb, 0u, eb, e0, tb, t0, scan);
+    for (int i = 0; i < per; ++i) {
+        const int r = r0 + i;
+        if (r < n && row_mode[r] == 1) {
+            const int64_t nl = fused_row_lists(rows, r, k_sink, k_swa, fused_cols);
+            for (int64_t c = 0; c < nl; ++c, ++eb)
+                if ((int64_t)eb < table_cap)
+                    table[2 * (int64_t)eb] = r, table[2 * (int64_t)eb + 1] = (int32_t)c;
+        }
+    }
+    if (threadIdx.x == 0)
+        counts[2] = (int32_t)((int64_t)tb < table_cap ? (int64_t)tb : table_cap);
 }
 
 hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
-                            uint8_t *row_mode, int32_t *lists, int32_t *counts, hipStream_t stream)
+                            uint8_t *row_mode, int32_t *lists, int32_t *counts, int k_sink, int k_swa,
+                            int64_t fused_cols, int32_t *table, int64_t table_cap, hipStream_t stream)
 {
     if (rows.n_rows == 0)
         return hipSuccess;
     hipLaunchKernelGGL(row_modes_kernel, dim3(1), dim3(kModeThreads), 0, stream, rows, idx_row, hi_min_len,
-                       hi_enabled, row_mode, lists, counts);
+                       hi_enabled, row_mode, lists, counts, k_sink, k_swa, fused_cols, table, table_cap);
     return hipGetLastError();
 }
 

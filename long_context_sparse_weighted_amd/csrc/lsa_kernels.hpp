@@ -12,11 +12,15 @@ namespace lsa {
 // Row gating for the layer: when row_mode != nullptr, only rows with row_mode[r] == want run.
 // list / count (optional, streaming scoring kernels only): the rows with row_mode[r] == want in ascending
 // order and their number, so that the blocks of those rows can be launched first.
+// table / table_count (optional, the fused flat pass only): its blocks that have work, as (row, chunk)
+// pairs in order, so that those come first and no block without work is launched among them.
 struct RowGate {
     const uint8_t *row_mode;
     int want;
     const int32_t *list = nullptr;
     const int32_t *count = nullptr;
+    const int32_t *table = nullptr;
+    const int32_t *table_count = nullptr;
 };
 
 // Per-row input sizes of the candidate-list levels after a fused first level (on = false: every row has
@@ -88,9 +92,12 @@ hipError_t launch_hybrid_attn(int dtype, const RowsDev &rows, const void *q, con
 
 // --- layer helpers (layer.hip)
 // Also writes, for modes 1 and 2, the rows of that mode in ascending order (lists [2][n_rows]) and their
-// numbers (counts[2]).
+// numbers (counts[0..1]); with fused_cols > 0 also the (row, chunk) pairs of the fused flat pass's blocks
+// that have work (table [2 * table_cap], fused_row_lists of each flat row, rows ascending) and their
+// number (counts[2]; at most table_cap).
 hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t hi_min_len, int hi_enabled,
-                            uint8_t *row_mode, int32_t *lists, int32_t *counts, hipStream_t stream);
+                            uint8_t *row_mode, int32_t *lists, int32_t *counts, int k_sink, int k_swa,
+                            int64_t fused_cols, int32_t *table, int64_t table_cap, hipStream_t stream);
 
 // Rounds a byte count up to the workspace alignment.
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -200,6 +200,22 @@ int lsa_index_topk_workspace_size(int dtype, const lsa_rows_t *rows, int32_t n_h
                                   int32_t k_sparse, size_t *bytes);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, hosts that forbid hipMalloc): lsa_index_topk with its workspace in a device array of the
+ * library, LSA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the first call on that GPU until
+ * the process ends.  Same arguments, result and errors as lsa_index_topk minus (ws, ws_bytes);
+ * rows whose lsa_index_topk_workspace_size() exceeds the array return LSA_ERR_UNSUPPORTED (64 MiB
+ * holds the fused selection of 32 bf16 decode rows at 1M tokens).  The stream must belong to the
+ * current device (else LSA_ERR_INVALID).  Allocates nothing.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (other streams, other host threads) race and must
+ * be serialised by the caller.
+ */
+#define LSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int lsa_index_topk_noalloc(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                           int32_t n_heads, int32_t head_dim, lsa_budget_t budget, int32_t *idx,
+                           hipStream_t stream);
+
+/*
  * Hybrid sparse attention over the MLA latent ([paper] §4.1.1 HFA; attention of [summary] "DSA
  * Mechanism Formalization"; latent layout [paper] §5.1 Table 6):
  *   S(r) = sink(t) u swa(t) u { idx[ir, i] : in mid(t), not equal to idx[ir, i-1] },

@@ -18,7 +18,7 @@ LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = r
 LSA_F32, LSA_BF16 = 0, 1
 
 SYMBOLS = ("lsa_index_score", "lsa_quantize_fp8", "lsa_index_score_fp8", "lsa_page_means", "lsa_page_means_append", "lsa_page_recall", "lsa_page_recall_workspace_size", "lsa_topk",
-           "lsa_topk_workspace_size", "lsa_index_topk", "lsa_index_topk_workspace_size",
+           "lsa_topk_workspace_size", "lsa_index_topk", "lsa_index_topk_workspace_size", "lsa_index_topk_noalloc",
            "lsa_index_topk_fp8", "lsa_index_topk_fp8_workspace_size", "lsa_hybrid_attn", "lsa_hybrid_attn_workspace_size", "lsa_layer_fwd",
            "lsa_layer_workspace_size", "lsa_status_string", "lsa_last_error")
 
@@ -69,6 +69,7 @@ def lib():
         L.lsa_topk_workspace_size.argtypes = [I32, I64, I32, ctypes.POINTER(SZ)]
         L.lsa_index_topk.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, P, SZ, P]
         L.lsa_index_topk_workspace_size.argtypes = [ctypes.c_int, RP, I32, I32, I32, ctypes.POINTER(SZ)]
+        L.lsa_index_topk_noalloc.argtypes = [ctypes.c_int, RP, P, P, P, I32, I32, Budget, P, P]
         L.lsa_index_topk_fp8.argtypes = [RP, P, P, P, P, P, I32, I32, Budget, P, P, SZ, P]
         L.lsa_index_topk_fp8_workspace_size.argtypes = [RP, I32, I32, I32, ctypes.POINTER(SZ)]
         L.lsa_hybrid_attn.argtypes = [ctypes.c_int, RP, P, P, I32, I32, I32, F, Budget, P, P, P, P, P, SZ, P]
@@ -275,6 +276,21 @@ def lsa_index_topk(rows: RowsDesc, q_idx, w, k_idx, budget, idx=None, ws=None):
         idx = torch.empty((n_rows, bud.k_sparse), dtype=torch.int32, device=q_idx.device)
     _check(lib().lsa_index_topk(dt, ctypes.byref(rows.c()), _p(q_idx), _p(w), _p(k_idx), HI, dI, bud, _p(idx), wp,
                                 wn, _stream()))
+    return idx
+
+
+def lsa_index_topk_noalloc(rows: RowsDesc, q_idx, w, k_idx, budget, idx=None):
+    """lsa_index_topk with the library's own device scratch array: no workspace argument, no device
+    allocation inside the call (idx must be passed in for that)."""
+    n_rows, HI, dI = q_idx.shape
+    dt = _dt(q_idx)
+    _need(k_idx, q_idx.dtype, "k_idx")
+    _need(w, torch.float32, "w")
+    bud = Budget(*budget)
+    if idx is None:
+        idx = torch.empty((n_rows, bud.k_sparse), dtype=torch.int32, device=q_idx.device)
+    _check(lib().lsa_index_topk_noalloc(dt, ctypes.byref(rows.c()), _p(q_idx), _p(w), _p(k_idx), HI, dI, bud,
+                                        _p(idx), _stream()))
     return idx
 
 

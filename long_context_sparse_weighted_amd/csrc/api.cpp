@@ -257,7 +257,41 @@ int check_layer_cfg(const lsa_layer_cfg_t *cfg)
     return LSA_OK;
 }
 
+int check_index_topk(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k)
+{
+    if (dtype != LSA_F32 && dtype != LSA_BF16)
+        return fail(LSA_ERR_INVALID, "dtype must be LSA_F32 or LSA_BF16");
+    if (int st = check_rows(rows))
+        return st;
+    if (!index_score_supported(dtype, n_heads, head_dim))
+        return fail(LSA_ERR_UNSUPPORTED, "indexer shape (%d heads, dim %d) not compiled for this dtype", n_heads,
+                    head_dim);
+    if (k < 1 || k > 4096)
+        return fail(LSA_ERR_UNSUPPORTED, "k_sparse must be in [1, 4096]");
+    return LSA_OK;
+}
+
 }  // namespace
+
+namespace lsa {
+
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
+int index_topk_check(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                     int n_heads, int head_dim, lsa_budget_t budget, const int32_t *idx, size_t *ws_bytes)
+{
+    if (int st = check_index_topk(dtype, rows, n_heads, head_dim, budget.k_sparse))
+        return st;
+    if (int st = check_budget(budget))
+        return st;
+    if (rows->n_rows > 0 && (!q_idx || !w || !k_idx || !idx))
+        return fail(LSA_ERR_INVALID, "q_idx, w, k_idx and idx must be device pointers");
+    size_t sb;
+    *ws_bytes = flat_select_bytes(dtype, rows, n_heads, head_dim, budget.k_sparse, &sb);
+    return LSA_OK;
+}
+
+}  // namespace lsa
 
 extern "C" {
 
@@ -594,20 +628,6 @@ int lsa_topk(int32_t n_rows, const float *scores, int64_t ld_scores, int64_t n_c
     return hip_status(e, "lsa_topk launch");
 }
 
-static int check_index_topk(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim, int32_t k)
-{
-    if (dtype != LSA_F32 && dtype != LSA_BF16)
-        return fail(LSA_ERR_INVALID, "dtype must be LSA_F32 or LSA_BF16");
-    if (int st = check_rows(rows))
-        return st;
-    if (!index_score_supported(dtype, n_heads, head_dim))
-        return fail(LSA_ERR_UNSUPPORTED, "indexer shape (%d heads, dim %d) not compiled for this dtype", n_heads,
-                    head_dim);
-    if (k < 1 || k > 4096)
-        return fail(LSA_ERR_UNSUPPORTED, "k_sparse must be in [1, 4096]");
-    return LSA_OK;
-}
-
 int lsa_index_topk_workspace_size(int dtype, const lsa_rows_t *rows, int32_t n_heads, int32_t head_dim,
                                   int32_t k_sparse, size_t *bytes)
 {
@@ -624,14 +644,9 @@ int lsa_index_topk(int dtype, const lsa_rows_t *rows, const void *q_idx, const f
                    int32_t n_heads, int32_t head_dim, lsa_budget_t budget, int32_t *idx, void *ws, size_t ws_bytes,
                    hipStream_t stream)
 {
-    if (int st = check_index_topk(dtype, rows, n_heads, head_dim, budget.k_sparse))
+    size_t need;
+    if (int st = lsa::index_topk_check(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, budget, idx, &need))
         return st;
-    if (int st = check_budget(budget))
-        return st;
-    if (rows->n_rows > 0 && (!q_idx || !w || !k_idx || !idx))
-        return fail(LSA_ERR_INVALID, "q_idx, w, k_idx and idx must be device pointers");
-    size_t sb;
-    const size_t need = flat_select_bytes(dtype, rows, n_heads, head_dim, budget.k_sparse, &sb);
     if (ws_bytes < need || (need && !ws))
         return fail(LSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", ws_bytes, need);
     if (ws && !aligned256(ws))

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/lsa.h"
 #include "lsa_dev.hpp"
 
 namespace lsa {
@@ -101,5 +102,13 @@ hipError_t launch_row_modes(const RowsDev &rows, const int32_t *idx_row, int64_t
 
 // Rounds a byte count up to the workspace alignment.
 inline size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Records msg as the calling thread's lsa_last_error() text and returns code.
+int set_error(int code, const char *msg);
+
+// The host-side checks of lsa_index_topk (errors recorded as lsa_last_error() text); on LSA_OK,
+// *ws_bytes is the workspace its launch needs.  Touches no HIP call.
+int index_topk_check(int dtype, const lsa_rows_t *rows, const void *q_idx, const float *w, const void *k_idx,
+                     int n_heads, int head_dim, lsa_budget_t budget, const int32_t *idx, size_t *ws_bytes);
 
 }  // namespace lsa

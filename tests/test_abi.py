@@ -164,6 +164,18 @@ def test_index_topk_validation_and_workspace(L):
     assert call(big, fake, sz.value, idx=None) == L.LSA_ERR_INVALID
     assert call(big, fake, sz.value, bud=L.Budget(-1, 1024, 1024)) == L.LSA_ERR_INVALID
     assert call(_rows(L, 1, 0, 0), None, 0) == L.LSA_OK                            # no rows: nothing to do
+    # the variant with the library's own scratch array: the same checks, then its size, before any HIP call
+    na = lambda r, dt=1, H=64, D=128, bud=b, idx=fake: lib.lsa_index_topk_noalloc(dt, ctypes.byref(r), fake, fake,
+                                                                                  fake, H, D, bud, idx, None)
+    assert sz.value <= 64 << 20                      # 32 decode rows at 1M fit the 64 MiB array
+    assert na(big, H=32) == L.LSA_ERR_UNSUPPORTED
+    assert na(big, bud=L.Budget(16, 1024, 4097)) == L.LSA_ERR_UNSUPPORTED
+    assert na(big, dt=5) == L.LSA_ERR_INVALID
+    assert na(big, idx=None) == L.LSA_ERR_INVALID
+    huge = _rows(L, 32, 32, 1 << 20)                 # fp32 rows score through the workspace: 128 MiB
+    assert na(huge, dt=0, H=4, D=64) == L.LSA_ERR_UNSUPPORTED
+    assert b"scratch" in lib.lsa_last_error()
+    assert na(_rows(L, 1, 0, 0)) == L.LSA_OK
 
 
 def test_index_topk_fp8_validation_and_workspace(L):

@@ -12,7 +12,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblsa.so")
+# LSA_LIB: another build of the same sources (e.g. the host-sanitizer build of the CPU tests)
+LIB_PATH = os.environ.get("LSA_LIB") or os.path.join(_HERE, "liblsa.so")
 
 LSA_OK, LSA_ERR_INVALID, LSA_ERR_UNSUPPORTED, LSA_ERR_WORKSPACE, LSA_ERR_HIP = range(5)
 LSA_F32, LSA_BF16 = 0, 1

@@ -16,10 +16,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, extra=()) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     objs = []
-    obj_dir = os.path.join(HERE, "_build")
+    obj_dir = os.path.join(HERE, "_build") if out == LIB else out + ".objs"
     os.makedirs(obj_dir, exist_ok=True)
     procs = []
     for src in sources():
@@ -40,15 +40,20 @@ def build(verbose: bool = False, extra=()) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
+    # python -m long_context_sparse_weighted_amd.build [--out PATH] [extra hipcc flags ...]
     import sys
-    print(build(verbose=True, extra=sys.argv[1:]))
+    args = sys.argv[1:]
+    dest = LIB
+    if args[:1] == ["--out"]:
+        dest, args = os.path.abspath(args[1]), args[2:]
+    print(build(verbose=True, extra=args, out=dest))

@@ -24,7 +24,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(_HERE, "liblsa_ref.so")
+        # LSA_ORACLE_LIB: another build of the same source (the sanitizer build of build.py --sanitize)
+        path = os.environ.get("LSA_ORACLE_LIB") or os.path.join(_HERE, "liblsa_ref.so")
         if not os.path.exists(path):
             _build.build()
         _lib = ctypes.CDLL(path)

@@ -149,6 +149,13 @@ int64_t flat_fused_segments(const lsa_rows_t *rows, int64_t ld, int64_t *cols)
     return (ld + *cols - 1) / *cols;
 }
 
+// The same for the FP8 fused pass, whose 16384-column form needs two blocks per CU.
+int64_t fp8_fused_segments(const lsa_rows_t *rows, int64_t ld, int64_t *cols)
+{
+    *cols = index_select_fused_cols_fp8(rows->n_rows, ld);
+    return (ld + *cols - 1) / *cols;
+}
+
 // Workspace of the flat selection (lsa_index_topk and the layer's flat rows): candidate lists of the
 // fused pass, or the scores and the top-K lists of the separate passes; the scores come first.
 size_t flat_select_bytes(int dtype, const lsa_rows_t *rows, int n_heads, int head_dim, int k, size_t *scores_bytes)
@@ -416,7 +423,7 @@ static size_t fp8_select_bytes(const lsa_rows_t *rows, int k, size_t *scores_byt
     if (fp8_fused(rows, k)) {
         *scores_bytes = 0;
         int64_t cols;
-        return topk_lists_workspace_bytes(rows->n_rows, flat_fused_segments(rows, ld, &cols), k);
+        return topk_lists_workspace_bytes(rows->n_rows, fp8_fused_segments(rows, ld, &cols), k);
     }
     *scores_bytes = align_up(sizeof(float) * (size_t)rows->n_rows * (size_t)ld);
     return *scores_bytes + topk_workspace_bytes(rows->n_rows, ld, k);
@@ -470,7 +477,7 @@ int lsa_index_topk_fp8(const lsa_rows_t *rows, const uint8_t *q8, const float *q
     hipError_t e;
     if (fp8_fused(rows, k)) {
         int64_t cols;
-        const int64_t n_seg = flat_fused_segments(rows, ld, &cols);
+        const int64_t n_seg = fp8_fused_segments(rows, ld, &cols);
         uint32_t *sk;
         int32_t *sp;
         int64_t sld;

@@ -336,6 +336,8 @@ __device__ inline void wait_vmcnt()
 // reused by the selection; the scores stay in registers): 80 KB, two blocks per CU.
 constexpr int kFusedCols = 8192;
 constexpr int kFusedRing = 5;
+// The 8-wave form (one block per CU): a 4-deep ring of 4 KB per wave, 128 KB per block.
+constexpr int kFusedRing8 = 4;
 
 // Block -> (row, chunk) of the streaming kernels.  Blocks go to the 8 XCDs in turn, in launch order
 // (chunk fastest), so chunk c of every row lands on the XCD of c mod 8.  The fused selection passes
@@ -424,24 +426,27 @@ constexpr int fused_lds_words(int C) { return C + 2 * (C / 32) + 16; }
 // columns (ties at the threshold in a second map, ranked by a scan over the map's words), and thread t
 // emits the picks of columns 32 t .. 32 t + 31.  The pairs (order key, position) go to chunk * k_sel
 // of row r's candidate list, padded with (0, -1).  lds: the block's idle ring, kFusedLdsWords words.
-template <int C>
-__device__ inline void fused_select_regs(const float (&s)[C / 256], uint32_t *lds, int64_t c_first, int64_t tile0,
+template <int C, int NT = 256>
+__device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds, int64_t c_first, int64_t tile0,
                                          int wave, int g, int n, int r, int64_t chunk, int k_sel,
                                          uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
                                          int64_t sel_ld)
 {
-    constexpr int kFusedV = C / 256;   // scores per thread
-    constexpr int kMapW = C / 32 / 256;  // bit-map words per thread
-    static_assert(kLdsWords + 16 <= fused_lds_words(C) && kMapW >= 1 && C % (32 * 256) == 0, "whole map words");
+    constexpr int kFusedV = C / NT;      // scores per thread
+    constexpr int kMapW = C / 32 / NT;   // bit-map words per thread
+    constexpr int kWaves = NT / kWave;
+    static_assert(kLdsWords + 3 * kWaves + 3 <= fused_lds_words(C) && 2 * kWaves <= 16 && kMapW >= 1 &&
+                      C % (32 * NT) == 0,
+                  "the select scratch fits below the epilogue's words; whole map words");
     __syncthreads();  // every wave's ring DMA has landed: the ring's LDS is free
     uint32_t key[kFusedV];
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m)
         key[m] = is_candidate(s[m]) ? float_order_key(s[m]) : 0u;
-    uint32_t *scratch = lds + kLdsWords;
-    int *s_d = reinterpret_cast<int *>(scratch + 12);
-    uint32_t *s_above = scratch + 13, *s_bin = scratch + 14;
-    const Selection sel = block_select<256, kFusedV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
+    uint32_t *scratch = lds + kLdsWords;  // 3 words per wave for the block reductions, then 3 more
+    int *s_d = reinterpret_cast<int *>(scratch + 3 * kWaves);
+    uint32_t *s_above = scratch + 3 * kWaves + 1, *s_bin = scratch + 3 * kWaves + 2;
+    const Selection sel = block_select<NT, kFusedV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
     // Thresholds on the whole key (as in block_emit): picked when x >= t_gt; a tie when x == t_eq.
     uint32_t t_gt, t_eq = 0xffffffffu;
     if (sel.all)
@@ -460,7 +465,7 @@ __device__ inline void fused_select_regs(const float (&s)[C / 256], uint32_t *ld
     for (int m = 0; m < kFusedV; ++m) {
         const uint32_t x = key[m];
         if (x >= t_gt || x == t_eq) {  // a candidate (key 0 never is): its column lies in the chunk
-            const uint32_t li = (uint32_t)((tile0 + 4 * (m * kWavesPerBlock + wave) + g) * kTile + n - c_first);
+            const uint32_t li = (uint32_t)((tile0 + 4 * (m * kWaves + wave) + g) * kTile + n - c_first);
             pkey[li] = x;
             atomicOr(x >= t_gt ? &gmap[li >> 5] : &emap[li >> 5], 1u << (li & 31));
         }
@@ -473,7 +478,7 @@ __device__ inline void fused_select_regs(const float (&s)[C / 256], uint32_t *ld
         cg += (uint32_t)__popc(gw[i]), ce += (uint32_t)__popc(ew[i]);
     }
     uint32_t bg, be, tg, te;
-    block_scan2<256>(cg, ce, bg, be, tg, te, scan);
+    block_scan2<NT>(cg, ce, bg, be, tg, te, scan);
     uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
     int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
     uint32_t slot = bg + (be < sel.k_rem ? be : sel.k_rem);  // picks at lower positions
@@ -497,8 +502,8 @@ __device__ inline void fused_select_regs(const float (&s)[C / 256], uint32_t *ld
     }
 }
 
-template <int MODE, int S, int SEL>
-__global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
+template <int MODE, int S, int SEL, int WV = kWavesPerBlock>
+__global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ keys, int k_sink, int k_swa,
                                                             const int32_t *__restrict__ pages, int M, int P,
@@ -511,9 +516,11 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
 {
     static_assert(S >= 2 && 4 * (S - 1) < 64, "ring depth");
     constexpr bool SELECT = SEL > 0;     // SEL: the fused pass's chunk width (0: write the scores)
-    constexpr int kFusedV = SELECT ? SEL / 256 : 1;
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kTile * kDim * 2 >= 4 * fused_lds_words(SEL)),
+    constexpr int kThreads = 64 * WV;    // WV waves (the selection runs on all of them)
+    constexpr int kFusedV = SELECT ? SEL / kThreads : 1;
+    static_assert(!SELECT || (MODE == kModeFlat && S * WV * kTile * kDim * 2 >= 4 * fused_lds_words(SEL)),
                   "the selection reuses the ring for its LDS");
+    static_assert(SELECT || WV == kWavesPerBlock, "the scoring form runs 4 waves");
     int r;
     int64_t chunk;
     if (blk_table) {
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
             return;  // scored by the multi-row kernel
     }
-    __shared__ __attribute__((aligned(16))) uint16_t ring[S][kWavesPerBlock][kTile * kDim];
+    __shared__ __attribute__((aligned(16))) uint16_t ring[S][WV][kTile * kDim];
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         // block reads one dense window; step k of this wave is tile k % 4 of its group k / 4.  Steps
         // past the wave's K use its last step's tile again (a tile past the chunk, in the last group,
         // re-reads the chunk's last tile).
-        constexpr int W = kWavesPerBlock;
+        constexpr int W = WV;
         const int64_t chunk_tile = c_begin / kTile;
         const int64_t end_tile = (c_end + kTile - 1) / kTile;
         const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         const int64_t safe_key = cm.base + cm.lo;
         const uint32_t ring_base =
             (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)&ring[0][wave][0];
-        constexpr uint32_t kSlotBytes = kWavesPerBlock * kTile * kDim * 2;
+        constexpr uint32_t kSlotBytes = WV * kTile * kDim * 2;
         // Token position of the first column of a tile (-1: the tile holds no token).  A tile lies in
         // one page (P is a multiple of 16), so the page table is read once per tile, by a scalar load.
         auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
@@ -756,7 +763,7 @@ __global__ __launch_bounds__(256) void score_stream_kernel(RowsDev rows, const u
         }
     }
     if constexpr (SELECT)
-        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r,
+        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r,
                                chunk, k_sel, sel_key, sel_pos, sel_ld);
 }
 
@@ -1549,12 +1556,21 @@ bool index_select_fusable(int dtype, int n_rows, int n_seq, int n_heads, int hea
 
 int64_t index_select_fused_segments(int64_t n_cols) { return (n_cols + kFusedCols - 1) / kFusedCols; }
 
-// Chunk width of the bf16 fused pass: 16384 columns once that still gives two blocks per CU (half the
-// blocks, so half the per-block q loads, prologues and candidate lists), else 8192.
+// Chunk width of the bf16 fused pass: 16384 columns once that gives every CU a block (half the blocks,
+// so half the per-block q loads, prologues and candidate lists, and half the candidates of the next
+// level), else 8192.
 int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols)
 {
     // (a batch of more than 64 rows is taken to be ragged: the chunks of its short rows are empty, so
     // n_rows x chunks overstates the work, and the narrower chunks keep two blocks per CU)
+    return n_rows < kMinGroupedRows && n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 256
+               ? 2 * kFusedCols
+               : kFusedCols;
+}
+
+// FP8: 16384 columns only while that still gives two blocks per CU (its 16384-column form runs 4 waves).
+int64_t index_select_fused_cols_fp8(int64_t n_rows, int64_t n_cols)
+{
     return n_rows < kMinGroupedRows && n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 512
                ? 2 * kFusedCols
                : kFusedCols;
@@ -1567,11 +1583,16 @@ hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, con
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
     dim3 grid((unsigned)((n_cols + cols - 1) / cols), (unsigned)rows.n_rows);
-    if (cols == 2 * kFusedCols)
+    if (cols == 2 * kFusedCols && (int64_t)grid.x * grid.y >= 512)  // two blocks of 4 waves per CU
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
                            rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1,
                            nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld,
                            gate.list, gate.count, gate.table, gate.table_count);
+    else if (cols == 2 * kFusedCols)  // one round of blocks: one block of 8 waves per CU
+        hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing8, 2 * kFusedCols, 8>), grid, dim3(512), 0,
+                           stream, rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0,
+                           1, nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
+                           sel_ld, gate.list, gate.count, gate.table, gate.table_count);
     else
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, kFusedCols>), grid, dim3(256), 0, stream, rows,
                            (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,

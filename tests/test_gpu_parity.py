@@ -474,8 +474,11 @@ def test_layer_bf16_decode_ragged():
 FUSED_LENGTHS = [1, 17, 1041, 1042, 3001, 8192, 8193, 20000, 40000, 200001]
 # (the last two rows sit at t = L_b: rows outside their sequence, which select nothing)
 FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9, 8192 + 1040), (6, 8193), (5, 8192)]
-# 42 rows x 13 chunks of 16384 columns: wide enough for the bf16 fused pass's 16384-column chunks
+# 42 rows x 13 chunks of 16384 columns (546 blocks): the bf16 fused pass on 16384-column chunks, two
+# 4-wave blocks per CU
 WIDE_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
+# 24 rows x 13 chunks (312 blocks, one round): 16384-column chunks, one 8-wave block per CU
+MID_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 9001 * i) for i in range(1, 11)]
 
 
 @pytest.mark.parametrize("distinct", [1, 3, 40])
@@ -483,7 +486,8 @@ def test_index_topk_fused_ties(distinct):
     # keys drawn from a few distinct vectors, so every row's scores tie in long runs and the picks at the
     # threshold are decided by position (1: all candidates equal); the fused pass (14 rows x 25
     # segments) must match scoring then selecting bit for bit
-    x = custom_rows(FUSED_LENGTHS, WIDE_FUSED_ROWS if distinct == 3 else FUSED_ROWS, attn=False, seed=46)
+    rows = {3: WIDE_FUSED_ROWS, 40: MID_FUSED_ROWS}.get(distinct, FUSED_ROWS)
+    x = custom_rows(FUSED_LENGTHS, rows, attn=False, seed=46)
     n_tok = x["k_idx"].shape[0]
     pick = torch.randint(0, distinct, (n_tok,), generator=synth.generator(47, DEV), device=DEV)
     x["k_idx"] = x["k_idx"][:distinct].clone()[pick].contiguous()
@@ -496,12 +500,13 @@ def test_index_topk_fused_ties(distinct):
         assert torch.equal(got, lsa.lsa_topk(sc, k))
 
 
-@pytest.mark.parametrize("wide", [False, True])
-def test_index_topk_fused_vs_oracle(wide):
+@pytest.mark.parametrize("form", ["8192", "16384x8w", "16384"])
+def test_index_topk_fused_vs_oracle(form):
     # The fused scoring + first top-K level against the oracle's whole-row selection (Eq. 1 over mid(t),
-    # then Eq. 2): 14 rows x 25 chunks take the 8192-column kernel, 42 rows x 13 chunks the 16384-column
-    # kernel that the 1M decode runs.  Index sets must agree except at near-ties of the oracle's ranking.
-    rows = WIDE_FUSED_ROWS if wide else FUSED_ROWS
+    # then Eq. 2): 14 rows x 25 chunks take the 8192-column kernel, 24 rows x 13 chunks the 16384-column
+    # 8-wave kernel that the 128K decode runs, 42 rows x 13 chunks the 16384-column 4-wave kernel that the
+    # 1M decode runs.  Index sets must agree except at near-ties of the oracle's ranking.
+    rows = {"8192": FUSED_ROWS, "16384x8w": MID_FUSED_ROWS, "16384": WIDE_FUSED_ROWS}[form]
     x = custom_rows(FUSED_LENGTHS, rows, attn=False, seed=61)
     o = oracle_inputs(x)
     c = x["cfg"]
@@ -512,8 +517,7 @@ def test_index_topk_fused_vs_oracle(wide):
         want = ref.topk(sc, k)
         theta = [kth_best(sc[r], k) for r in range(len(rows))]
         n_diff = assert_idx_sets_match(got, want, lambda r, d: near_tie(sc[r][d], theta[r]), f"fused k={k}")
-        log(f"fused selection ({'16384' if wide else '8192'}-column chunks) k={k}: {n_diff} rows with near-tie "
-            f"differences")
+        log(f"fused selection ({form}) k={k}: {n_diff} rows with near-tie differences")
 
 
 def test_layer_fused_first_level_equals_separate_passes():
@@ -534,7 +538,7 @@ def test_index_topk_equals_score_then_topk(k):
     # lsa_index_topk on the fused pass (14 rows x 25 segments of 8192 columns) and on the separate
     # passes (2 rows) against scoring everything and then selecting: bit-identical index sets
     for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 42), (FUSED_LENGTHS, WIDE_FUSED_ROWS, 51),
-                                ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
+                                (FUSED_LENGTHS, MID_FUSED_ROWS, 52), ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
         x = custom_rows(lengths, rows, attn=False, seed=seed)
         c = x["cfg"]
         bud = (c["k_sink"], c["k_swa"], k)

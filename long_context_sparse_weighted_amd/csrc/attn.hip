@@ -833,14 +833,25 @@ constexpr int kMaxSplit = kMaxSplitMerge;
 // split count minimises rounds x (tiles per split + 5), with at least 4 tiles per split.
 static int pick_split(int n_rows, int n_heads, int k_total)
 {
+    // Time model in units of one 32-row tile step of a block (about 2.4-3.2 us): a launch takes
+    // rounds x (tiles per split + 5) units (5 for a block's fixed costs: q loads, pick compaction, the
+    // first tile's latency, the output stores), and with ns > 1 the merge kernel adds its launch
+    // (about 2.5 us) and its traffic (the bf16 partials read and the output written, at about
+    // 4.4 TB/s).  Measured: 8 rows take 13 splits, 32 rows 8, 64 rows 4; 192 rows (a ragged batch of
+    // drafts) run unsplit, where 4 splits cost 183 + 25 us of merge.
     const int64_t row_blocks = (int64_t)n_rows * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
     const int n_tiles = (k_total + kRowsPerTile - 1) / kRowsPerTile;
     const int max_split = min(kMaxSplit, max(1, n_tiles / 4));
+    constexpr double kUnitUs = 2.8;
     int best = 1;
-    int64_t best_cost = INT64_MAX;
+    double best_cost = 1e300;
     for (int ns = 1; ns <= max_split; ++ns) {
         const int64_t rounds = (row_blocks * ns + 255) / 256;
-        const int64_t cost = rounds * ((n_tiles + ns - 1) / ns + 5);
+        double cost = (double)(rounds * ((n_tiles + ns - 1) / ns + 5));
+        if (ns > 1) {
+            const double bytes = (double)n_rows * n_heads * ((double)ns * (kDv * 2 + 8) + kDv * 2);
+            cost += (2.5 + bytes / 4.4e6) / kUnitUs;
+        }
         if (cost < best_cost) {
             best_cost = cost;
             best = ns;

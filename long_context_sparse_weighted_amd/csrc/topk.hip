@@ -261,6 +261,10 @@ hipError_t launch_topk(int n_rows, const float *scores, int64_t ld, int64_t n_co
             hipLaunchKernelGGL((topk_level_kernel<kSmallThreads, kSmallVpt, true, true>), dim3(1, n_rows),
                                dim3(kSmallThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
                                nullptr, nullptr, 0, idx, gate.row_mode, gate.want, ListCount{}, 0);
+        else if (n_cols <= kFinalVpt * kSegThreads)  // at most 8192 columns (the page recall at 1M, P = 128)
+            hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kFinalVpt, true, true>), dim3(1, n_rows),
+                               dim3(kSegThreads), 0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k,
+                               nullptr, nullptr, 0, idx, gate.row_mode, gate.want, ListCount{}, 0);
         else
             hipLaunchKernelGGL((topk_level_kernel<kSegThreads, kVpt, true, true>), dim3(1, n_rows), dim3(kSegThreads),
                                0, stream, scores, ld, n_cols, pages, M, P, nullptr, nullptr, 0, k, nullptr, nullptr, 0,

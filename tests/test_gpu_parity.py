@@ -144,7 +144,8 @@ def _score_rows(rng, n_rows, n_cols, kind):
 @pytest.mark.parametrize("n_rows,n_cols,K,kind", [
     (3, 1, 1, "gauss"), (5, 100, 7, "gauss"), (4, 100, 200, "ties"), (4, 5000, 1024, "gauss"),
     (4, 5000, 1024, "ties"), (3, 20000, 1024, "quant"), (2, 70000, 1024, "equal"), (1, 4096, 4096, "quant"),
-    (64, 3000, 112, "gauss"), (2, 300000, 1024, "quant")])
+    (64, 3000, 112, "gauss"), (2, 300000, 1024, "quant"), (3, 8192, 1024, "quant"), (2, 8193, 1024, "gauss"),
+    (2, 8192, 4096, "ties")])
 def test_topk_bit_exact_on_oracle_style_scores(n_rows, n_cols, K, kind):
     rng = np.random.default_rng(n_rows * 7919 + n_cols + K)
     s = _score_rows(rng, n_rows, n_cols, kind)

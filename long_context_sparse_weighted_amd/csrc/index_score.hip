@@ -117,7 +117,8 @@ constexpr int kTile = 16;          // keys per MFMA tile
 constexpr int kWavesPerBlock = 4;
 
 // Rows 16 G .. 16 G + 15 form group G.  A group is scored by the multi-row kernel when all of its
-// rows exist, lie inside one sequence and pass the row gate: the rows then read the same keys.
+// rows exist and pass the row gate and its rows that lie inside their sequence (the others are empty
+// rows, all -inf) share one sequence: the rows then read the same keys.
 constexpr int kGroupRows = 16;
 
 __device__ inline bool group_uniform(const RowsDev &rows, const uint8_t *row_mode, int want, int grp)
@@ -125,21 +126,31 @@ __device__ inline bool group_uniform(const RowsDev &rows, const uint8_t *row_mod
     const int r0 = grp * kGroupRows;
     if (r0 + kGroupRows > rows.n_rows)
         return false;
-    const int32_t b = rows.row_seq[r0];
-    if (b < 0 || b >= rows.n_seq)
-        return false;
-    const int64_t L = rows.kv_off[b + 1] - rows.kv_off[b];
+    int32_t b = -1;
     for (int i = 0; i < kGroupRows; ++i) {
         const int r = r0 + i;
-        if (rows.row_seq[r] != b)
-            return false;
-        const int32_t t = rows.row_pos[r];
-        if (t < 0 || t >= L)
-            return false;
         if (row_mode && row_mode[r] != want)
+            return false;
+        const RowInfo ri = row_info(rows, r);
+        if (!ri.valid)
+            continue;
+        if (b < 0)
+            b = ri.seq;
+        else if (ri.seq != b)
             return false;
     }
     return true;
+}
+
+// The sequence of a group's rows that lie inside it (-1: every row of the group is empty).
+__device__ inline int32_t group_seq(const RowsDev &rows, int grp)
+{
+    for (int i = 0; i < kGroupRows; ++i) {
+        const RowInfo ri = row_info(rows, grp * kGroupRows + i);
+        if (ri.valid)
+            return ri.seq;
+    }
+    return -1;
 }
 
 template <int MODE>
@@ -1091,12 +1102,16 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
     // Column ranges (columns are below 2^31): every valid row scores [lo, hi_r) -- flat: from k_sink to
     // the end of its mid region cut at L; page-mean: the sub-blocks of its causal pages -- and lanes
     // 0..15 of every wave take one row each and reduce.
-    const RowInfo ri0 = row_info(rows, grp * kGroupRows);
-    int L = (int)ri0.L;    // keys of the sequence
-    int64_t base = ri0.base;
-    if constexpr (MODE == kModePageMean) {
-        base = sb_off[ri0.seq];
-        L = (int)(sb_off[ri0.seq + 1] - base);
+    const int32_t gseq = group_seq(rows, grp);  // (-1: no row scores anything, every column is -inf)
+    int L = 0;         // keys of the sequence
+    int64_t base = 0;
+    if (gseq >= 0) {
+        base = rows.kv_off[gseq];
+        L = (int)(rows.kv_off[gseq + 1] - base);
+        if constexpr (MODE == kModePageMean) {
+            base = sb_off[gseq];
+            L = (int)(sb_off[gseq + 1] - base);
+        }
     }
     const int n_keys = L;
     auto last_page = [&](const RowInfo &ri) {  // causal pages p <= floor(t / P) that exist
@@ -1163,7 +1178,8 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
         const int kk0 = 4 * wave + g;
         const int c16 = n ^ (kk0 & 15);
         const uint16_t *kseq = keys + base * kDim;
-        const int my_last_page = MODE == kModePageMean ? last_page(row_info(rows, r)) : 0;
+        const RowInfo my_ri = row_info(rows, r);
+        const int my_last_page = MODE == kModePageMean && my_ri.valid ? last_page(my_ri) : -1;  // -1: empty row
         auto issue_stage = [&](int st, uint16_t *buf) __attribute__((always_inline)) {
             const int col0 = c_begin + st * kStageKeys;
             const uint16_t *ks0 = kseq + (int64_t)col0 * kDim;
@@ -1427,6 +1443,9 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
     if (dtype == 1) {
         const ScoreGeom geo = score_geometry(rows.n_rows, n_cols);
         const bool grouped = (MODE == kModeFlat || MODE == kModePageMean) && rows.n_rows >= kMinGroupedRows;
+        // One sequence, whole groups, no gate: every group is uniform, so the per-row launch would only
+        // find rows already scored (a prefill chunk: 73,728 blocks returning at once, 0.3 ms).
+        const bool all_grouped = grouped && rows.n_seq == 1 && rows.n_rows % kGroupRows == 0 && !gate.row_mode;
         if constexpr (MODE == kModeFlat || MODE == kModePageMean) {
             if (grouped) {
                 dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
@@ -1435,7 +1454,9 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
                                    scores, ld, n_cols, geo.chunk_elems, gate.row_mode, gate.want);
             }
         }
-        if constexpr (MODE == kModePageMean) {
+        if (all_grouped) {
+            // (nothing left for the per-row kernels)
+        } else if constexpr (MODE == kModePageMean) {
             dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
             hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
                                (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,

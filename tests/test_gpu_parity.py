@@ -71,7 +71,8 @@ def test_index_score_bf16_ragged_and_edges():
 # Rows that exercise the multi-row (prefill) scoring kernel: groups of 16 rows of one sequence are
 # scored together, other groups row by row.  Groups: 0 uniform; 1 uniform with empty and edge mid
 # regions; 2 alternating sequences; 3 uniform in the second sequence; 4 uniform in a sequence too
-# short for any mid region; 5 with one row outside its sequence; then a partial group of 5 rows.
+# short for any mid region; 5 with one row outside its sequence; 6 whose first row lies outside another
+# sequence; 7 with every row outside its sequence; then a partial group of 5 rows.
 GROUPED_LENGTHS = [6000, 3000, 700]
 GROUPED_ROWS = ([(0, t) for t in range(5984, 6000)]
                 + [(0, t) for t in (0, 1, 15, 16, 1039, 1040, 1041, 1042, 2000, 2001, 3000, 4500, 5999, 5998, 100,
@@ -80,7 +81,13 @@ GROUPED_ROWS = ([(0, t) for t in range(5984, 6000)]
                 + [(1, t) for t in range(2984, 3000)]
                 + [(2, t) for t in range(684, 700)]
                 + [(0, t) for t in range(3000, 3015)] + [(0, 6000)]
+                + [(1, 3000)] + [(0, t) for t in range(4100, 4115)]
+                + [(2, 700 + 3 * i) for i in range(16)]
                 + [(0, t) for t in range(4000, 4005)])
+# One sequence in whole groups (every group is scored by the multi-row kernel, no per-row launch), with
+# rows outside the sequence (t >= L) inside the groups and a group of them only.
+SINGLE_SEQ_ROWS = ([(0, t) for t in range(4900, 4916)] + [(0, 5000 + t if t % 5 == 0 else 4800 + t) for t in range(16)]
+                   + [(0, 5000 + t) for t in range(16)] + [(0, t) for t in range(1030, 1046)])
 
 
 def test_index_score_bf16_grouped_rows():
@@ -93,6 +100,17 @@ def test_index_score_bf16_grouped_rows():
                            c["k_swa"], ld=ld)
     log("grouped bf16 scores worst err/tol", assert_scores_close(host(g), want))
     assert np.all(np.isneginf(host(g)[64:80]))   # L = 700: no mid region anywhere
+
+
+def test_index_score_bf16_single_sequence_groups():
+    x = custom_rows([5000], SINGLE_SEQ_ROWS, attn=False, seed=33)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c))
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=5000)
+    log("single-sequence groups worst err/tol", assert_scores_close(host(g), want))
+    assert np.all(np.isneginf(host(g)[32:48]))   # rows past the sequence: no scores
 
 
 def test_layer_bf16_grouped_rows():
@@ -253,7 +271,27 @@ def test_page_recall_scores_and_pages(B):
 PM_LENGTHS = [20100, 9000]
 PM_ROWS = ([(0, t) for t in range(19940, 20004)]          # 4 uniform groups over the page edge at 19968
            + [(0, t) for t in range(20084, 20100)]        # a group ending in the partial last page
+           + [(1, 9000)] + [(0, t) for t in range(20000, 20015)]  # first row outside its (other) sequence
            + [(1, 8999), (0, 5000), (1, 4000), (0, 20099), (1, 127), (0, 0), (1, 200)])
+
+
+@pytest.mark.parametrize("B", [8, 128])
+def test_page_scores_single_sequence_groups(B):
+    # one sequence in whole groups: no per-row launch; rows past the sequence come out all -inf
+    L = 20100
+    rows = [(0, t) for t in range(19940, 19988)] + [(0, L + t if t % 4 == 0 else 19900 + t) for t in range(16)]
+    x = custom_rows([L], rows, attn=False, seed=14)
+    o = oracle_inputs(x)
+    P, M = 128, 40
+    sb_off = lsa.sb_offsets([L], B)
+    km_o = ref.page_means(o["kv_off"], sb_off.numpy(), o["k_idx"], B)
+    km = synth.bits_to_bf16(km_o).to(DEV)
+    ld = (L + P - 1) // P + 3
+    ps = torch.empty((len(rows), ld), dtype=torch.float32, device=DEV)
+    lsa.lsa_page_recall(rows_of(x), sb_off.to(DEV), x["q_idx"], x["w"], km, P, B, M, page_scores=ps)
+    want_ps = ref.page_scores(o["kv_off"], sb_off.numpy(), o["row_seq"], o["row_pos"], o["q_idx"], o["w"], km_o, P,
+                              B, ld)
+    log("single-sequence page scores worst err/tol", assert_scores_close(host(ps), want_ps, "page scores"))
 
 
 @pytest.mark.parametrize("B", [8, 128, 32])

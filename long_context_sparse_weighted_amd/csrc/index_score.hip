@@ -121,36 +121,31 @@ constexpr int kWavesPerBlock = 4;
 // rows, all -inf) share one sequence: the rows then read the same keys.
 constexpr int kGroupRows = 16;
 
+// The 16 rows are read at once, one per lane (lanes 16 .. 63 repeat them), and combined by ballots:
+// the answer is the same in every wave.
 __device__ inline bool group_uniform(const RowsDev &rows, const uint8_t *row_mode, int want, int grp)
 {
     const int r0 = grp * kGroupRows;
     if (r0 + kGroupRows > rows.n_rows)
         return false;
-    int32_t b = -1;
-    for (int i = 0; i < kGroupRows; ++i) {
-        const int r = r0 + i;
-        if (row_mode && row_mode[r] != want)
-            return false;
-        const RowInfo ri = row_info(rows, r);
-        if (!ri.valid)
-            continue;
-        if (b < 0)
-            b = ri.seq;
-        else if (ri.seq != b)
-            return false;
-    }
-    return true;
+    const int r = r0 + (lane_id() & (kGroupRows - 1));
+    const bool gated_out = row_mode && row_mode[r] != want;
+    const RowInfo ri = row_info(rows, r);
+    if (__ballot(gated_out) != 0)
+        return false;
+    const uint64_t valid = __ballot(ri.valid);
+    if (valid == 0)
+        return true;
+    const int32_t b = __shfl(ri.seq, __ffsll((long long)valid) - 1, kWave);
+    return __ballot(ri.valid && ri.seq != b) == 0;
 }
 
 // The sequence of a group's rows that lie inside it (-1: every row of the group is empty).
 __device__ inline int32_t group_seq(const RowsDev &rows, int grp)
 {
-    for (int i = 0; i < kGroupRows; ++i) {
-        const RowInfo ri = row_info(rows, grp * kGroupRows + i);
-        if (ri.valid)
-            return ri.seq;
-    }
-    return -1;
+    const RowInfo ri = row_info(rows, grp * kGroupRows + (lane_id() & (kGroupRows - 1)));
+    const uint64_t valid = __ballot(ri.valid);
+    return valid == 0 ? -1 : __shfl(ri.seq, __ffsll((long long)valid) - 1, kWave);
 }
 
 template <int MODE>

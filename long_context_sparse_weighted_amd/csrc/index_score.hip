@@ -798,6 +798,7 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
 #endif
 constexpr int kFp8Ring = LSA_FP8_RING;
 constexpr int kFp8WideRing = 8;  // the 16384-column fused pass: its epilogue needs 68 KB of the ring
+// (the 8-wave form of that pass: 8 x 8 slots of 2304 B, 144 KB, one block per CU)
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kDim8 = 128;                          // bytes per key (E4M3 codes of d_I = 128)
 constexpr int kTileCodes8 = kTile * kDim8;          // 2 KB
@@ -816,8 +817,8 @@ __device__ inline void dma_4(const void *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
-template <int MODE, int S, int SEL>
-__global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
+template <int MODE, int S, int SEL, int WV = kWavesPerBlock>
+__global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
                                                          const float *__restrict__ q_scale,
                                                          const float *__restrict__ w, const uint8_t *__restrict__ k8,
                                                          const float *__restrict__ k_scale, int k_sink, int k_swa,
@@ -828,13 +829,15 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
 {
     static_assert(S >= 2 && 3 * (S - 1) < 64, "ring depth");
     constexpr bool SELECT = SEL > 0;  // SEL: the fused pass's chunk width (0: write the scores)
-    constexpr int kFusedV = SELECT ? SEL / 256 : 1;
-    static_assert(!SELECT || (MODE == kModeFlat && S * kWavesPerBlock * kSlot8 >= 4 * fused_lds_words(SEL)),
+    constexpr int kThreads = 64 * WV;  // WV waves (the selection runs on all of them)
+    constexpr int kFusedV = SELECT ? SEL / kThreads : 1;
+    static_assert(SELECT || WV == kWavesPerBlock, "the scoring form runs 4 waves");
+    static_assert(!SELECT || (MODE == kModeFlat && S * WV * kSlot8 >= 4 * fused_lds_words(SEL)),
                   "the selection reuses the ring for its LDS");
     int r;
     int64_t chunk;
     stream_block<MODE, MODE == kModePaged || SELECT>(r, chunk);
-    __shared__ __attribute__((aligned(16))) uint8_t ring[S][kWavesPerBlock][kSlot8];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[S][WV][kSlot8];
     float sreg[kFusedV];  // SELECT: this lane's scores, one per group of four tiles
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m)
@@ -868,7 +871,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     } else if (empty) {  // no keys here: publish the empty candidate list
-        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
+        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
                           sel_key, sel_pos, sel_ld);
         return;
     }
@@ -896,7 +899,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
             loaded_here(wv[mt][i]);
     }
 
-    constexpr int W = kWavesPerBlock;
+    constexpr int W = WV;
     const int64_t chunk_tile = c_begin / kTile;
     const int64_t end_tile = (c_end + kTile - 1) / kTile;
     const int64_t n_groups = (end_tile - chunk_tile + 3) / 4;
@@ -907,7 +910,7 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
     const int64_t safe_key = cm.base + cm.lo;
     const uint32_t ring_base =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)&ring[0][wave][0];
-    constexpr uint32_t kRingStep = kWavesPerBlock * kSlot8;
+    constexpr uint32_t kRingStep = WV * kSlot8;
     auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
         const int64_t c0 = tile * kTile;
         if constexpr (MODE == kModeFlat) {
@@ -1034,19 +1037,20 @@ __global__ __launch_bounds__(256) void score_fp8_kernel(RowsDev rows, const uint
         wait_vmcnt<0>();
     }
     if constexpr (SELECT)
-        fused_select_regs<SEL>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
+        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
                           k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)
-#define LSA_FP8_INSTANCE(MODE, RING, SEL)                                                                           \
-    template __global__ void score_fp8_kernel<MODE, RING, SEL>(                                                        \
+#define LSA_FP8_INSTANCE(MODE, RING, SEL, WV)                                                                       \
+    template __global__ void score_fp8_kernel<MODE, RING, SEL, WV>(                                                    \
         RowsDev, const uint8_t *, const float *, const float *, const uint8_t *, const float *, int, int,             \
         const int32_t *, int, int, float *, int64_t, int64_t, int64_t, int, uint32_t *, int32_t *, int64_t);
-LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, 0)
-LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0)
-LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, kFusedCols)
-LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, 0, 4)
+LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0, 4)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, kFusedCols, 4)
+LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 4)
+LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 8)
 #undef LSA_FP8_INSTANCE
 
 // ------------------------------------------------------------------------------------------
@@ -1536,8 +1540,12 @@ hipError_t launch_index_select_fused_fp8(const RowsDev &rows, const uint8_t *q8,
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
     dim3 grid((unsigned)((n_cols + cols - 1) / cols), (unsigned)rows.n_rows);
-    if (cols == 2 * kFusedCols)
-        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8WideRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
+    if (cols == 2 * kFusedCols && (int64_t)grid.x * grid.y >= 512)  // two blocks of 4 waves per CU
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8WideRing, 2 * kFusedCols, 4>), grid, dim3(256), 0, stream,
+                           rows, q8, q_scale, w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols,
+                           cols, k, sel_key, sel_pos, sel_ld);
+    else if (cols == 2 * kFusedCols)  // one round of blocks: one block of 8 waves per CU
+        hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8WideRing, 2 * kFusedCols, 8>), grid, dim3(512), 0, stream,
                            rows, q8, q_scale, w, k8, k_scale, k_sink, k_swa, nullptr, 0, 1, nullptr, (int64_t)0, n_cols,
                            cols, k, sel_key, sel_pos, sel_ld);
     else
@@ -1584,10 +1592,10 @@ int64_t index_select_fused_cols(int64_t n_rows, int64_t n_cols)
                : kFusedCols;
 }
 
-// FP8: 16384 columns only while that still gives two blocks per CU (its 16384-column form runs 4 waves).
+// FP8: the same rule (the 16384-column pass also has a one-round, 8-wave form).
 int64_t index_select_fused_cols_fp8(int64_t n_rows, int64_t n_cols)
 {
-    return n_rows < kMinGroupedRows && n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 512
+    return n_rows < kMinGroupedRows && n_rows * ((n_cols + 2 * kFusedCols - 1) / (2 * kFusedCols)) >= 256
                ? 2 * kFusedCols
                : kFusedCols;
 }

@@ -421,17 +421,25 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
 // its chunk's best k_sel (key desc, position asc) as the first-level candidate list of the top-K
 // (sel_key / sel_pos [row][chunk * k_sel ..], key 0 / position -1 padded), so the fp32 scores never go
 // to HBM (their write traffic, interleaved with the key stream, slowed the stream by ~15 % at 1M).
-// LDS words of the fused epilogue for C-column chunks: keys by position, two bit maps, scan scratch.
-constexpr int fused_lds_words(int C) { return C + 2 * (C / 32) + 16; }
+// LDS words of the fused epilogue for C-column chunks: the selection's histograms and scratch, or the
+// emit's (group, wave) counts, scan scratch and staged list (at most min(kMaxLocalK, C) picks).
+constexpr int fused_emit_words(int C) { return 2 * (C / kWave) + 16 + 2 * (C < kMaxLocalK ? C : kMaxLocalK); }
+constexpr int fused_lds_words(int C)
+{
+    return kLdsWords + 3 * 16 + 3 > fused_emit_words(C) ? kLdsWords + 3 * 16 + 3 : fused_emit_words(C);
+}
 
 // Epilogue of the fused scoring kernels, on scores held in registers: thread (wave w, lane (g, n)) holds
-// in s[j] the score of column (tile0 + 4 (4 j + w) + g) * 16 + n, i.e. of its j-th group of four tiles
-// (-inf where that column holds no key or lies past the chunk's key range).  Selects the k_sel best
-// under (score desc, position asc) with the block radix select, then writes them in position order:
-// every pick is put at its position in an LDS array and flagged in a bit map over the chunk's 8192
-// columns (ties at the threshold in a second map, ranked by a scan over the map's words), and thread t
-// emits the picks of columns 32 t .. 32 t + 31.  The pairs (order key, position) go to chunk * k_sel
-// of row r's candidate list, padded with (0, -1).  lds: the block's idle ring, kFusedLdsWords words.
+// in s[j] the score of column (tile0 + 4 (4 j + w) + g) * 16 + n (W waves: 4 (W j + w)), i.e. of its j-th
+// group of four tiles (-inf where that column holds no key or lies past the chunk's key range).  Selects
+// the k_sel best under (score desc, position asc) with the block radix select, then writes them in
+// position order.  For a fixed j, wave w's 64 lanes hold 64 consecutive columns, lane order being column
+// order, and those runs follow one another in (j, w) order: so ballots count the picks of each (j, w),
+// a block scan over the counts in that order gives each run its first slot, and a lane adds the picks
+// of the lanes below it.  Ties at the threshold are ranked the same way, in a second count.  The picks
+// are staged in LDS at their slots and the list goes out in coalesced stores: the pairs (order key,
+// position) at chunk * k_sel of row r's candidate list, padded with (0, -1).  lds: the block's idle
+// ring, fused_lds_words(C) words.
 template <int C, int NT = 256>
 __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds, int64_t c_first, int64_t tile0,
                                          int wave, int g, int n, int r, int64_t chunk, int k_sel,
@@ -439,11 +447,11 @@ __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds
                                          int64_t sel_ld)
 {
     constexpr int kFusedV = C / NT;      // scores per thread
-    constexpr int kMapW = C / 32 / NT;   // bit-map words per thread
     constexpr int kWaves = NT / kWave;
-    static_assert(kLdsWords + 3 * kWaves + 3 <= fused_lds_words(C) && 2 * kWaves <= 16 && kMapW >= 1 &&
-                      C % (32 * NT) == 0,
-                  "the select scratch fits below the epilogue's words; whole map words");
+    constexpr int kE = kFusedV * kWaves;  // (group, wave) runs of 64 columns
+    constexpr int kStage = C < kMaxLocalK ? C : kMaxLocalK;
+    static_assert(2 * kWaves <= 16 && kFusedV <= kWave && kE <= NT && C % NT == 0,
+                  "a lane per group's count; a thread per run in the scan");
     __syncthreads();  // every wave's ring DMA has landed: the ring's LDS is free
     uint32_t key[kFusedV];
 #pragma unroll
@@ -461,51 +469,56 @@ __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds
         t_gt = sel.prefix << (32 - sel.consumed);
     else
         t_gt = sel.prefix + 1u, t_eq = sel.prefix;
-    uint32_t *pkey = lds, *gmap = lds + C, *emap = gmap + C / 32, *scan = emap + C / 32;
-    __syncthreads();  // the selection's LDS is no longer read
-#pragma unroll
-    for (int i = 0; i < kMapW; ++i)
-        gmap[kMapW * threadIdx.x + i] = emap[kMapW * threadIdx.x + i] = 0u;
-    __syncthreads();
+    uint32_t *cnt = lds, *scan = lds + 2 * kE, *stage_key = scan + 16, *stage_pos = stage_key + kStage;
+    const int lane = lane_id();
+    // picks (cg) and ties (ce) of run (m, wave), held by lane m
+    uint32_t cg = 0, ce = 0;
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m) {
-        const uint32_t x = key[m];
-        if (x >= t_gt || x == t_eq) {  // a candidate (key 0 never is): its column lies in the chunk
-            const uint32_t li = (uint32_t)((tile0 + 4 * (m * kWaves + wave) + g) * kTile + n - c_first);
-            pkey[li] = x;
-            atomicOr(x >= t_gt ? &gmap[li >> 5] : &emap[li >> 5], 1u << (li & 31));
+        // (the empty asm ties key m to the counts so far: otherwise the compiler issues all the
+        // independent ballots first and holds their masks in scalar registers, which spill)
+        uint32_t x = key[m];
+        asm volatile("" : "+v"(x), "+v"(cg), "+v"(ce));
+        const uint32_t ng = (uint32_t)__popcll(__ballot(x >= t_gt)), ne = (uint32_t)__popcll(__ballot(x == t_eq));
+        cg = lane == m ? ng : cg;
+        ce = lane == m ? ne : ce;
+    }
+    __syncthreads();  // the selection's LDS is no longer read
+    if (lane < kFusedV)
+        cnt[lane * kWaves + wave] = cg, cnt[kE + lane * kWaves + wave] = ce;
+    __syncthreads();
+    const int t = (int)threadIdx.x;
+    const uint32_t rg = t < kE ? cnt[t] : 0u, re = t < kE ? cnt[kE + t] : 0u;
+    uint32_t bg, be, tg, te;
+    block_scan2<NT>(rg, re, bg, be, tg, te, scan);  // (its barriers order the reads above before the writes)
+    if (t < kE)
+        cnt[t] = bg, cnt[kE + t] = be;
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t slot = 0;
+#pragma unroll
+    for (int m = 0; m < kFusedV; ++m) {
+        uint32_t x = key[m];
+        asm volatile("" : "+v"(x), "+v"(slot));  // (one ballot pair at a time, as above)
+        const bool gt = x >= t_gt, eq = x == t_eq;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint32_t e_before = cnt[kE + m * kWaves + wave] + (uint32_t)__popcll(me & below);
+        slot = cnt[m * kWaves + wave] + (uint32_t)__popcll(mg & below) + (e_before < sel.k_rem ? e_before : sel.k_rem);
+        if (gt || (eq && e_before < sel.k_rem)) {
+            stage_key[slot] = x;
+            stage_pos[slot] = (int32_t)((tile0 + 4 * (m * kWaves + wave) + g) * kTile + n);
         }
     }
     __syncthreads();
-    uint32_t gw[kMapW], ew[kMapW], cg = 0, ce = 0;
-#pragma unroll
-    for (int i = 0; i < kMapW; ++i) {
-        gw[i] = gmap[kMapW * threadIdx.x + i], ew[i] = emap[kMapW * threadIdx.x + i];
-        cg += (uint32_t)__popc(gw[i]), ce += (uint32_t)__popc(ew[i]);
-    }
-    uint32_t bg, be, tg, te;
-    block_scan2<NT>(cg, ce, bg, be, tg, te, scan);
+    const uint32_t n_sel = tg + (te < sel.k_rem ? te : sel.k_rem);
     uint32_t *kout = sel_key + (int64_t)r * sel_ld + chunk * k_sel;
     int32_t *pout = sel_pos + (int64_t)r * sel_ld + chunk * k_sel;
-    uint32_t slot = bg + (be < sel.k_rem ? be : sel.k_rem);  // picks at lower positions
-    uint32_t e_seen = be;
-#pragma unroll
-    for (int i = 0; i < kMapW; ++i)
-        for (int b = 0; b < 32; ++b) {
-            const bool gb = (gw[i] >> b) & 1u, eb = (ew[i] >> b) & 1u;
-            if (gb || (eb && e_seen < sel.k_rem)) {
-                const uint32_t li = 32u * (kMapW * threadIdx.x + i) + (uint32_t)b;
-                kout[slot] = pkey[li];
-                pout[slot] = (int32_t)(c_first + li);
-                ++slot;
-            }
-            e_seen += eb ? 1u : 0u;
-        }
-    const uint32_t n_sel = tg + (te < sel.k_rem ? te : sel.k_rem);
-    for (uint32_t i = n_sel + threadIdx.x; i < (uint32_t)k_sel; i += blockDim.x) {
-        kout[i] = 0u;
-        pout[i] = -1;
+    for (uint32_t i = (uint32_t)t; i < (uint32_t)k_sel; i += NT) {
+        const bool in = i < n_sel;
+        kout[i] = in ? stage_key[i] : 0u;
+        pout[i] = in ? (int32_t)stage_pos[i] : -1;
     }
+    (void)c_first;
 }
 
 template <int MODE, int S, int SEL, int WV = kWavesPerBlock>

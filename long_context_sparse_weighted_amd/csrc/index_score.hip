@@ -429,48 +429,52 @@ constexpr int fused_lds_words(int C)
     return kLdsWords + 3 * 16 + 3 > fused_emit_words(C) ? kLdsWords + 3 * 16 + 3 : fused_emit_words(C);
 }
 
-// Epilogue of the fused scoring kernels, on scores held in registers: thread (wave w, lane (g, n)) holds
-// in s[j] the score of column (tile0 + 4 (4 j + w) + g) * 16 + n (W waves: 4 (W j + w)), i.e. of its j-th
-// group of four tiles (-inf where that column holds no key or lies past the chunk's key range).  Selects
-// the k_sel best under (score desc, position asc) with the block radix select, then writes them in
-// position order.  For a fixed j, wave w's 64 lanes hold 64 consecutive columns, lane order being column
-// order, and those runs follow one another in (j, w) order: so ballots count the picks of each (j, w),
-// a block scan over the counts in that order gives each run its first slot, and a lane adds the picks
-// of the lanes below it.  Ties at the threshold are ranked the same way, in a second count.  The picks
-// are staged in LDS at their slots and the list goes out in coalesced stores: the pairs (order key,
-// position) at chunk * k_sel of row r's candidate list, padded with (0, -1).  lds: the block's idle
-// ring, fused_lds_words(C) words.
-template <int C, int NT = 256>
-__device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds, int64_t c_first, int64_t tile0,
-                                         int wave, int g, int n, int r, int64_t chunk, int k_sel,
-                                         uint32_t *__restrict__ sel_key, int32_t *__restrict__ sel_pos,
-                                         int64_t sel_ld)
+// Order key of a score for the selection (0: not a candidate).
+__device__ __attribute__((always_inline)) inline uint32_t select_key(float v)
 {
-    constexpr int kFusedV = C / NT;      // scores per thread
+    return is_candidate(v) ? float_order_key(v) : 0u;
+}
+
+// v_mbcnt: the set bits of mask in the lanes below this one.
+__device__ __attribute__((always_inline)) inline uint32_t lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Epilogue of the fused scoring kernels, on keys held in registers (built while the chunk streams, with
+// their statistics st): thread (wave w, lane (g, n)) holds in key[j] the order key of the score of
+// column (tile0 + 4 (W j + w) + g) * 16 + n (W waves), i.e. of its j-th group of four tiles (0 where
+// that column holds no key or lies past the chunk's key range).  Selects the k_sel best under
+// (score desc, position asc) with the block radix select, then writes them in position order.  For a
+// fixed j, wave w's 64 lanes hold 64 consecutive columns, lane order being column order, and those runs
+// follow one another in (j, w) order: so ballots count the picks of each (j, w), a block scan over the
+// counts in that order gives each run its first slot, and a lane adds the picks of the lanes below it.
+// Ties at the threshold (rare: only when the k-th key's value repeats past k) are ranked the same way,
+// in a second count.  The picks are staged in LDS at their slots and the list goes out in coalesced
+// stores: the pairs (order key, position) at chunk * k_sel of row r's candidate list, padded with
+// (0, -1).  lds: the block's idle ring, fused_lds_words(C) words.
+template <int C, int NT = 256>
+__device__ inline void fused_select_regs(const uint32_t (&key)[C / NT], KeyStats st, uint32_t *lds, int64_t tile0,
+                                         int wave, int r, int64_t chunk, int k_sel, uint32_t *__restrict__ sel_key,
+                                         int32_t *__restrict__ sel_pos, int64_t sel_ld)
+{
+    constexpr int kFusedV = C / NT;      // keys per thread
     constexpr int kWaves = NT / kWave;
     constexpr int kE = kFusedV * kWaves;  // (group, wave) runs of 64 columns
     constexpr int kStage = C < kMaxLocalK ? C : kMaxLocalK;
     static_assert(2 * kWaves <= 16 && kFusedV <= kWave && kE <= NT && C % NT == 0,
                   "a lane per group's count; a thread per run in the scan");
     __syncthreads();  // every wave's ring DMA has landed: the ring's LDS is free
-    uint32_t key[kFusedV];
-#pragma unroll
-    for (int m = 0; m < kFusedV; ++m)
-        key[m] = is_candidate(s[m]) ? float_order_key(s[m]) : 0u;
     uint32_t *scratch = lds + kLdsWords;  // 3 words per wave for the block reductions, then 3 more
     int *s_d = reinterpret_cast<int *>(scratch + 3 * kWaves);
     uint32_t *s_above = scratch + 3 * kWaves + 1, *s_bin = scratch + 3 * kWaves + 2;
-    const Selection sel = block_select<NT, kFusedV>(key, (uint32_t)k_sel, lds, scratch, s_d, s_above, s_bin);
-    // Thresholds on the whole key (as in block_emit): picked when x >= t_gt; a tie when x == t_eq.
-    uint32_t t_gt, t_eq = 0xffffffffu;
-    if (sel.all)
-        t_gt = 1u;
-    else if (sel.whole)
-        t_gt = sel.prefix << (32 - sel.consumed);
-    else
-        t_gt = sel.prefix + 1u, t_eq = sel.prefix;
+    const Selection sel = block_select<NT, kFusedV>(key, (uint32_t)k_sel, st, lds, scratch, s_d, s_above, s_bin);
+    // picked when x >= t_gt; a tie when x == t_eq (the first sel.k_rem ties in position order)
+    const uint32_t t_gt = sel.t_gt, t_eq = sel.t_eq;
+    const bool ties = t_eq != 0xffffffffu;  // (uniform)
     uint32_t *cnt = lds, *scan = lds + 2 * kE, *stage_key = scan + 16, *stage_pos = stage_key + kStage;
     const int lane = lane_id();
+    const uint32_t pos0 = (uint32_t)(tile0 * kTile) + 64u * (uint32_t)wave + (uint32_t)lane;  // column of key[0]
     // picks (cg) and ties (ce) of run (m, wave), held by lane m
     uint32_t cg = 0, ce = 0;
 #pragma unroll
@@ -479,9 +483,12 @@ __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds
         // independent ballots first and holds their masks in scalar registers, which spill)
         uint32_t x = key[m];
         asm volatile("" : "+v"(x), "+v"(cg), "+v"(ce));
-        const uint32_t ng = (uint32_t)__popcll(__ballot(x >= t_gt)), ne = (uint32_t)__popcll(__ballot(x == t_eq));
+        const uint32_t ng = (uint32_t)__popcll(__ballot(x >= t_gt));
         cg = lane == m ? ng : cg;
-        ce = lane == m ? ne : ce;
+        if (ties) {
+            const uint32_t ne = (uint32_t)__popcll(__ballot(x == t_eq));
+            ce = lane == m ? ne : ce;
+        }
     }
     __syncthreads();  // the selection's LDS is no longer read
     if (lane < kFusedV)
@@ -494,19 +501,32 @@ __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds
     if (t < kE)
         cnt[t] = bg, cnt[kE + t] = be;
     __syncthreads();
-    const uint64_t below = (1ull << lane) - 1ull;
     uint32_t slot = 0;
+    if (!ties) {
 #pragma unroll
-    for (int m = 0; m < kFusedV; ++m) {
-        uint32_t x = key[m];
-        asm volatile("" : "+v"(x), "+v"(slot));  // (one ballot pair at a time, as above)
-        const bool gt = x >= t_gt, eq = x == t_eq;
-        const uint64_t mg = __ballot(gt), me = __ballot(eq);
-        const uint32_t e_before = cnt[kE + m * kWaves + wave] + (uint32_t)__popcll(me & below);
-        slot = cnt[m * kWaves + wave] + (uint32_t)__popcll(mg & below) + (e_before < sel.k_rem ? e_before : sel.k_rem);
-        if (gt || (eq && e_before < sel.k_rem)) {
-            stage_key[slot] = x;
-            stage_pos[slot] = (int32_t)((tile0 + 4 * (m * kWaves + wave) + g) * kTile + n);
+        for (int m = 0; m < kFusedV; ++m) {
+            uint32_t x = key[m];
+            asm volatile("" : "+v"(x), "+v"(slot));  // (one ballot at a time, as above)
+            const bool gt = x >= t_gt;
+            slot = cnt[m * kWaves + wave] + lanes_below(__ballot(gt));
+            if (gt) {
+                stage_key[slot] = x;
+                stage_pos[slot] = pos0 + (uint32_t)(64 * kWaves * m);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < kFusedV; ++m) {
+            uint32_t x = key[m];
+            asm volatile("" : "+v"(x), "+v"(slot));  // (as above)
+            const bool gt = x >= t_gt, eq = x == t_eq;
+            const uint64_t mg = __ballot(gt), me = __ballot(eq);
+            const uint32_t e_before = cnt[kE + m * kWaves + wave] + lanes_below(me);
+            slot = cnt[m * kWaves + wave] + lanes_below(mg) + (e_before < sel.k_rem ? e_before : sel.k_rem);
+            if (gt || (eq && e_before < sel.k_rem)) {
+                stage_key[slot] = x;
+                stage_pos[slot] = pos0 + (uint32_t)(64 * kWaves * m);
+            }
         }
     }
     __syncthreads();
@@ -518,7 +538,6 @@ __device__ inline void fused_select_regs(const float (&s)[C / NT], uint32_t *lds
         kout[i] = in ? stage_key[i] : 0u;
         pout[i] = in ? (int32_t)stage_pos[i] : -1;
     }
-    (void)c_first;
 }
 
 template <int MODE, int S, int SEL, int WV = kWavesPerBlock>
@@ -594,11 +613,12 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     }
-    // SELECT: this lane's scores, one per group of four tiles (see fused_select_regs)
-    float sreg[kFusedV];
+    // SELECT: the order keys of this lane's scores, one per group of four tiles (see fused_select_regs)
+    uint32_t skey[kFusedV];
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m)
-        sreg[m] = -INFINITY;
+        skey[m] = 0u;
+    KeyStats st;
     int64_t sel_tile0 = 0;
     if (!empty) {  // (SELECT: a block without keys still publishes its empty candidate list below)
         u32x4 qa[4][4];
@@ -750,21 +770,23 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
             for (int k = 0; k < S; ++k)
                 issue(k);
             if constexpr (SELECT) {
-                // The scores stay in registers: groups in runs of 8 (register indices fixed at compile
-                // time), each run copied to its place in sreg by a wave-uniform branch.
+                // The scores stay in registers, as order keys (their conversion and statistics are
+                // VALU work the key stream hides): groups in runs of 8 (register indices fixed at
+                // compile time), each run copied to its place in skey by a wave-uniform branch.
                 for (int64_t j0 = 0; 4 * j0 < K; j0 += 8) {
-                    float part[8];
+                    uint32_t part[8];
     #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) {
                         int64_t c;
-                        part[jj] = 4 * (j0 + jj) < K ? group(4 * (j0 + jj), c) : -INFINITY;
+                        part[jj] = 4 * (j0 + jj) < K ? select_key(group(4 * (j0 + jj), c)) : 0u;
+                        st.add(part[jj]);
                     }
     #pragma unroll
                     for (int o = 0; o < kFusedV / 8; ++o)
                         if (j0 == 8 * o) {
     #pragma unroll
                             for (int jj = 0; jj < 8; ++jj)
-                                sreg[8 * o + jj] = part[jj];
+                                skey[8 * o + jj] = part[jj];
                         }
                 }
             } else {
@@ -782,8 +804,8 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
         }
     }
     if constexpr (SELECT)
-        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, sel_tile0, wave, g, n, r,
-                               chunk, k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs<SEL, kThreads>(skey, st, reinterpret_cast<uint32_t *>(&ring[0][0][0]), sel_tile0, wave, r, chunk,
+                                         k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -851,10 +873,11 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
     int64_t chunk;
     stream_block<MODE, MODE == kModePaged || SELECT>(r, chunk);
     __shared__ __attribute__((aligned(16))) uint8_t ring[S][WV][kSlot8];
-    float sreg[kFusedV];  // SELECT: this lane's scores, one per group of four tiles
+    uint32_t skey[kFusedV];  // SELECT: the order keys of this lane's scores, one per group of four tiles
 #pragma unroll
     for (int m = 0; m < kFusedV; ++m)
-        sreg[m] = -INFINITY;
+        skey[m] = 0u;
+    KeyStats st;
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
     const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
@@ -884,8 +907,8 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
         for (int64_t c = c_end + threadIdx.x; c < c_last; c += blockDim.x)
             out[c] = -INFINITY;
     } else if (empty) {  // no keys here: publish the empty candidate list
-        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, 0, wave, g, n, r, chunk, k_sel,
-                          sel_key, sel_pos, sel_ld);
+        fused_select_regs<SEL, kThreads>(skey, st, reinterpret_cast<uint32_t *>(&ring[0][0][0]), 0, wave, r, chunk, k_sel,
+                                         sel_key, sel_pos, sel_ld);
         return;
     }
     // A operand of head block mt: lane (n, g) holds bytes 32 g .. 32 g + 31 of head 16 mt + n; the key
@@ -1023,20 +1046,21 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
         for (int k = 0; k < S; ++k)
             issue(k);
         if constexpr (SELECT) {
-            // The scores stay in registers (as in the bf16 fused kernel).
+            // The scores stay in registers as order keys (as in the bf16 fused kernel).
             for (int64_t j0 = 0; 4 * j0 < K; j0 += 8) {
-                float part[8];
+                uint32_t part[8];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     int64_t c;
-                    part[jj] = 4 * (j0 + jj) < K ? group(4 * (j0 + jj), c) : -INFINITY;
+                    part[jj] = 4 * (j0 + jj) < K ? select_key(group(4 * (j0 + jj), c)) : 0u;
+                    st.add(part[jj]);
                 }
 #pragma unroll
                 for (int o = 0; o < kFusedV / 8; ++o)
                     if (j0 == 8 * o) {
 #pragma unroll
                         for (int jj = 0; jj < 8; ++jj)
-                            sreg[8 * o + jj] = part[jj];
+                            skey[8 * o + jj] = part[jj];
                     }
             }
         } else {
@@ -1050,8 +1074,8 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
         wait_vmcnt<0>();
     }
     if constexpr (SELECT)
-        fused_select_regs<SEL, kThreads>(sreg, reinterpret_cast<uint32_t *>(&ring[0][0][0]), c_first, chunk_tile, wave, g, n, r, chunk,
-                          k_sel, sel_key, sel_pos, sel_ld);
+        fused_select_regs<SEL, kThreads>(skey, st, reinterpret_cast<uint32_t *>(&ring[0][0][0]), chunk_tile, wave, r, chunk,
+                                         k_sel, sel_key, sel_pos, sel_ld);
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)

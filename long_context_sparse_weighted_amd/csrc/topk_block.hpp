@@ -86,50 +86,64 @@ __device__ __attribute__((always_inline)) inline void block_reduce3(uint32_t &cn
     __syncthreads();
 }
 
+// The result of a selection, as thresholds on the whole key: a key x is picked when x >= t_gt, and of the
+// keys equal to t_eq the first k_rem in position order are picked (t_eq = 0xffffffff, which no key
+// takes, when there are none to rank).  Every candidate is picked when `all` (t_gt = 1).
 struct Selection {
-    uint32_t prefix;    // fixed top `consumed` bits of the threshold
-    int consumed;
-    uint32_t k_rem;     // keys equal to the threshold that are picked (first in position order)
-    bool whole;         // keys whose top bits equal the prefix are all picked
-    bool all;           // every candidate is picked
+    uint32_t t_gt;
+    uint32_t t_eq;
+    uint32_t k_rem;
+    bool all;
 };
 
-// Radix select of the block's best k among the non-zero keys (0 = not a candidate).  The digit
-// histograms live in LDS as kCopies interleaved copies (bin b, copy c at hist[kCopies b + c]; lane l
-// adds to copy l % kCopies): keys of one row crowd into a few bins, and the copies spread the
-// atomics on such a bin over consecutive banks.  Keys that do not take part add to a per-lane
-// dummy word instead (no branch per key).
+// Radix select of the block's best k among the non-zero keys (0 = not a candidate), on the range the
+// keys actually take: every candidate lies in [kmin, kmax], so the search keeps an interval
+// [lo, lo + 2^s) that holds the k-th key, starting from lo = kmin and the least s with
+// kmax - kmin < 2^s, and each pass splits it into 2^11 bins by the digit (x - lo) >> (s - 11).
+// (Indexer scores of one block span a few binades: digits of a common bit prefix would be mostly
+// exponent bits and put the keys into a few bins, serialising the histogram atomics, and need a second
+// pass every time.)  Once the bin that holds the k-th key holds at most 64 keys, one wave ranks them.
+// The digit histograms live in LDS as kCopies interleaved copies (bin b, copy c at hist[kCopies b + c];
+// lane l adds to copy l % kCopies), so the atomics on a crowded bin go to consecutive banks.  In the
+// first pass the keys outside the interval (the zeros) add to a per-lane dummy word (no branch per
+// key); later passes count only the keys of the previous bin, by a branch.
 constexpr int kCopies = 2;
 constexpr int kHistWords = kBins * kCopies + kWave;  // + one dummy word per lane
 constexpr int kStageWords = 2 * (kMaxLocalK + kWave);
 constexpr int kLdsWords = kHistWords > kStageWords ? kHistWords : kStageWords;
 
+// A thread's count of candidates, its least candidate key less one (0xffffffff when it has none: the
+// key 0 wraps round) and its largest key, gathered key by key.
+struct KeyStats {
+    uint32_t cnt = 0u, low_m1 = 0xffffffffu, high = 0u;
+    __device__ __attribute__((always_inline)) void add(uint32_t x)
+    {
+        cnt += x != 0u ? 1u : 0u;
+        low_m1 = min(low_m1, x - 1u);
+        high = max(high, x);
+    }
+};
+
+// The selection on keys whose per-thread statistics are given (st: this thread's keys').
 template <int NT, int VPT>
-__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[VPT], uint32_t k,
+__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[VPT], uint32_t k, KeyStats st,
                                                                  uint32_t *hist, uint32_t *scratch, int *s_d,
                                                                  uint32_t *s_above, uint32_t *s_bin)
 {
-    Selection sel{0u, 0, k, false, false};
-    uint32_t total = 0, kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-    for (int m = 0; m < VPT; ++m) {
-        const uint32_t x = key[m];
-        total += x != 0 ? 1u : 0u;
-        kmin = min(kmin, x != 0 ? x : 0xffffffffu);
-        kmax = max(kmax, x);
-    }
+    Selection sel{1u, 0xffffffffu, k, false};
+    uint32_t total = st.cnt, kmin = st.low_m1, kmax = st.high;
     block_reduce3<NT>(total, kmin, kmax, scratch);
+    kmin += 1u;  // (a candidate exists whenever it is used below)
     if (total <= k) {
         sel.all = true;
         return sel;
     }
-    // Every candidate lies in [kmin, kmax], so it shares their common leading bits: the digits start
-    // below them.  (The candidates of a later level, the best keys of their segments, sit in a narrow
-    // range whose fixed top digits would pile them into a few bins.)
-    sel.consumed = kmin == kmax ? 32 : __clz(kmin ^ kmax);
-    sel.prefix = sel.consumed == 0 ? 0u : kmin >> (32 - sel.consumed);
-    if (sel.consumed == 32)
-        return sel;  // all candidates equal: the first k in position order
+    if (kmin == kmax) {  // all candidates equal: the first k in position order
+        sel.t_gt = kmin + 1u, sel.t_eq = kmin;
+        return sel;
+    }
+    uint32_t lo = kmin;
+    int s = 32 - __clz(kmax - kmin);  // kmax - lo < 2^s, 1 <= s <= 32
     const uint32_t lane = (uint32_t)lane_id();
     const uint32_t copy = lane % kCopies, dummy = kBins * kCopies + lane;
     constexpr int kPer = kBins / NT;  // bins owned by a thread in the suffix scan
@@ -137,26 +151,29 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
     for (int i = threadIdx.x; i < kBins * kCopies / 4; i += NT)
         reinterpret_cast<uint4 *>(hist)[i] = uint4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int pass = 0; pass < 3 && sel.consumed < 32; ++pass) {
-        const int width = min(kDigitBits, 32 - sel.consumed);
-        const int shift = 32 - sel.consumed - width;
-        const uint32_t dmask = (1u << width) - 1;
-        // keys whose top `consumed` bits equal the prefix: (x & pmask) == pval (uniform scalars)
-        const uint32_t pmask = sel.consumed == 0 ? 0u : ~0u << (32 - sel.consumed);
-        const uint32_t pval = sel.consumed == 0 ? 0u : sel.prefix << (32 - sel.consumed);
-        // Key 0 (not a candidate) can match only a zero prefix in pass 0, and then its digit is 0 while
-        // a candidate's is not (a candidate's top 11 bits are never all zero -- that would make it -inf
-        // or a NaN -- and with a zero prefix they all lie in the digit): its add goes to the dummy word
-        // like those of keys outside the prefix, so segments padded with zeros do not pile their
-        // atomics onto one bin.  (The test is on the digit, which changes with the pass, not on the
-        // key: the compiler would keep 64 loop-invariant key tests in scalar registers.)
-        const uint32_t keep0 = (pass != 0 || pval != 0u) ? 1u : 0u;
+    // x in [lo, lo + 2^s) after the first pass (s <= 21): x - lo < 2^s in 32 bits, since for a key below
+    // lo (a zero too) x - lo wraps to at least 2^32 - lo >= 2^23 (lo <= 0xff800000, the largest
+    // candidate key)
+    auto inside = [](uint32_t x, uint32_t l, int w) __attribute__((always_inline)) { return x - l < (1u << w); };
+    for (int pass = 0; pass < 3; ++pass) {
+        const int width = min(kDigitBits, s);
+        const int shift = s - width;
+        if (pass == 0) {
+            // every candidate lies in the first interval: only the zeros stay out
 #pragma unroll
-        for (int m = 0; m < VPT; ++m) {
-            const uint32_t x = key[m];
-            const uint32_t d = (x >> shift) & dmask;
-            const bool take = (x & pmask) == pval && (d | keep0) != 0u;
-            atomicAdd(&hist[take ? kCopies * d + copy : dummy], 1u);
+            for (int m = 0; m < VPT; ++m) {
+                uint32_t x = key[m];
+                asm volatile("" : "+v"(x));  // (opaque: keeps each compare mask in its own iteration)
+                atomicAdd(&hist[x != 0u ? kCopies * ((x - lo) >> shift) + copy : dummy], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < VPT; ++m) {
+                uint32_t x = key[m];
+                asm volatile("" : "+v"(x));  // (as above)
+                if (inside(x, lo, s))
+                    atomicAdd(&hist[kCopies * ((x - lo) >> shift) + copy], 1u);
+            }
         }
         __syncthreads();
         // Suffix sums (keys in bin b or above): thread t owns bins [kPer t, kPer t + kPer).
@@ -198,14 +215,69 @@ __device__ __attribute__((always_inline)) Selection block_select(const uint32_t 
         const uint32_t above = *s_above, bin = *s_bin;
         __syncthreads();
         sel.k_rem -= above;
-        sel.prefix = (sel.prefix << width) | (uint32_t)d;
-        sel.consumed += width;
-        if (bin == sel.k_rem) {
-            sel.whole = true;
-            break;
+        lo += (uint32_t)d << shift;
+        s = shift;
+        if (bin == sel.k_rem) {  // the bin is picked whole: every key >= lo
+            sel.t_gt = lo;
+            return sel;
+        }
+        if (s == 0) {  // the bin is one key value: ties, ranked by position
+            sel.t_gt = lo + 1u, sel.t_eq = lo;
+            return sel;
+        }
+        if (bin <= (uint32_t)kWave) {
+            // One wave ranks the bin's keys, gathered in the histogram words (all zero after a pass;
+            // hist[kWave] counts them).  The k_rem-th largest of them, T, is the threshold: the keys
+            // above T are picked, and of those equal to T the first k_rem - (the bin's keys above T).
+#pragma unroll
+            for (int m = 0; m < VPT; ++m) {
+                uint32_t x = key[m];
+                asm volatile("" : "+v"(x));  // (as above)
+                if (inside(x, lo, s)) {
+                    const uint32_t slot = atomicAdd(&hist[kWave], 1u);
+                    if (slot < (uint32_t)kWave)  // (always: the bin holds at most 64 keys)
+                        hist[slot] = x;
+                }
+            }
+            __syncthreads();
+            if (threadIdx.x < kWave) {
+                const uint32_t v = lane < bin ? hist[lane] : 0u;  // (0 lies below every key of the bin)
+                uint32_t gt = 0, ge = 0;
+                for (int j = 0; j < (int)bin; ++j) {
+                    const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+                    gt += u > v ? 1u : 0u;
+                    ge += u >= v ? 1u : 0u;
+                }
+                // T: a key of the bin with gt < k_rem <= ge (1 <= k_rem < bin; the lanes past the bin
+                // have gt = bin); every key equal to T is taken when ge = k_rem
+                const uint64_t hit = __ballot(lane < bin && gt < sel.k_rem && sel.k_rem <= ge);
+                if (lane == (uint32_t)(__ffsll((long long)hit) - 1))
+                    *s_above = v, *s_bin = gt, *s_d = ge == sel.k_rem ? 1 : 0;
+            }
+            __syncthreads();
+            const uint32_t t = *s_above;
+            sel.k_rem -= *s_bin;
+            if (*s_d)
+                sel.t_gt = t;  // (no ties to rank)
+            else
+                sel.t_gt = t + 1u, sel.t_eq = t;
+            __syncthreads();  // (the callers' next LDS writes may reuse these words)
+            return sel;
         }
     }
-    return sel;
+    return sel;  // (not reached: s reaches 0 within three passes)
+}
+
+template <int NT, int VPT>
+__device__ __attribute__((always_inline)) Selection block_select(const uint32_t (&key)[VPT], uint32_t k,
+                                                                 uint32_t *hist, uint32_t *scratch, int *s_d,
+                                                                 uint32_t *s_above, uint32_t *s_bin)
+{
+    KeyStats st;
+#pragma unroll
+    for (int m = 0; m < VPT; ++m)
+        st.add(key[m]);
+    return block_select<NT, VPT>(key, k, st, hist, scratch, s_d, s_above, s_bin);
 }
 
 // Writes the picks of a selection, in position order, to stage_key / stage_li (key and index in
@@ -217,17 +289,8 @@ __device__ __attribute__((always_inline)) uint32_t block_emit(const uint32_t (&k
                                                               uint32_t *stage_li, uint32_t first_li)
 {
     // Thresholds on the whole key (uniform): picked for sure when x >= t_gt; a tie when x == t_eq.
-    //   all: every candidate;  whole: keys with top bits >= prefix;  otherwise T is exact
-    //   (32 bits fixed): x > T picked, x == T a tie.
     //   (0xffffffff is a NaN pattern, mapped to key 0: no key equals it.)
-    uint32_t t_gt, t_eq = 0xffffffffu;
-    if (sel.all) {
-        t_gt = 1u;
-    } else if (sel.whole) {
-        t_gt = sel.prefix << (32 - sel.consumed);
-    } else {
-        t_gt = sel.prefix + 1u, t_eq = sel.prefix;  // consumed == 32: prefix is T
-    }
+    const uint32_t t_gt = sel.t_gt, t_eq = sel.t_eq;
     const uint32_t dummy = kMaxLocalK + (uint32_t)lane_id();
     if (t_eq == 0xffffffffu) {
         // No ties to resolve (the usual case: the threshold bin was taken whole): the picks are the

@@ -153,6 +153,15 @@ def _score_rows(rng, n_rows, n_cols, kind):
         s = rng.choice(np.array([-2.0, -0.0, 0.0, 0.5, 1.0, 3.0, np.inf], np.float32), (n_rows, n_cols))
     elif kind == "equal":
         s = np.full((n_rows, n_cols), 0.75, np.float32)
+    elif kind.startswith("pos"):  # positive, over two binades like indexer scores (optionally quantised):
+        # the first digit pass leaves a small bin of several values, with ties when quantised
+        s = (1.0 + 3.0 * rng.random((n_rows, n_cols))).astype(np.float32)
+        if kind != "pos":
+            step = int(kind[3:])
+            s = (np.round(s * step) / step).astype(np.float32)
+    elif kind.startswith("fine"):  # finely quantised: a few equal keys per value, also near the threshold
+        step = int(kind[4:])
+        s = (np.round(rng.standard_normal((n_rows, n_cols)) * step) / step).astype(np.float32)
     else:  # coarse quantised values: many ties at the threshold
         s = (rng.integers(-50, 50, (n_rows, n_cols)) / 8.0).astype(np.float32)
     s[rng.random((n_rows, n_cols)) < 0.1] = -np.inf
@@ -163,7 +172,9 @@ def _score_rows(rng, n_rows, n_cols, kind):
     (3, 1, 1, "gauss"), (5, 100, 7, "gauss"), (4, 100, 200, "ties"), (4, 5000, 1024, "gauss"),
     (4, 5000, 1024, "ties"), (3, 20000, 1024, "quant"), (2, 70000, 1024, "equal"), (1, 4096, 4096, "quant"),
     (64, 3000, 112, "gauss"), (2, 300000, 1024, "quant"), (3, 8192, 1024, "quant"), (2, 8193, 1024, "gauss"),
-    (2, 8192, 4096, "ties")])
+    (2, 8192, 4096, "ties"), (4, 16384, 1024, "fine256"), (4, 16384, 1024, "fine2048"), (2, 70000, 1024, "fine256"),
+    (3, 5000, 100, "fine2048"), (2, 300000, 1024, "fine4096"), (6, 16384, 1024, "pos"), (6, 16384, 1024, "pos4096"),
+    (4, 8192, 1024, "pos8192"), (3, 70000, 1024, "pos4096"), (2, 300000, 1024, "pos8192"), (4, 5000, 37, "pos4096")])
 def test_topk_bit_exact_on_oracle_style_scores(n_rows, n_cols, K, kind):
     rng = np.random.default_rng(n_rows * 7919 + n_cols + K)
     s = _score_rows(rng, n_rows, n_cols, kind)
@@ -520,12 +531,13 @@ WIDE_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
 MID_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 9001 * i) for i in range(1, 11)]
 
 
-@pytest.mark.parametrize("distinct", [1, 3, 40])
+@pytest.mark.parametrize("distinct", [1, 3, 40, 4096])
 def test_index_topk_fused_ties(distinct):
     # keys drawn from a few distinct vectors, so every row's scores tie in long runs and the picks at the
-    # threshold are decided by position (1: all candidates equal); the fused pass (14 rows x 25
-    # segments) must match scoring then selecting bit for bit
-    rows = {3: WIDE_FUSED_ROWS, 40: MID_FUSED_ROWS}.get(distinct, FUSED_ROWS)
+    # threshold are decided by position (1: all candidates equal; 4096: a few equal scores per value, so
+    # the threshold's digit bin is small but holds ties); the fused pass (14 rows x 25 segments) must
+    # match scoring then selecting bit for bit
+    rows = {3: WIDE_FUSED_ROWS, 40: MID_FUSED_ROWS, 4096: MID_FUSED_ROWS}.get(distinct, FUSED_ROWS)
     x = custom_rows(FUSED_LENGTHS, rows, attn=False, seed=46)
     n_tok = x["k_idx"].shape[0]
     pick = torch.randint(0, distinct, (n_tok,), generator=synth.generator(47, DEV), device=DEV)

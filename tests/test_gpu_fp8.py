@@ -12,8 +12,8 @@ import synth
 from oracle import fp8
 from parity_util import (assert_idx_sets_match, assert_scores_close, budget_of, f64, host, kth_best, log, near_tie,
                          oracle_inputs, rows_of)
-from test_gpu_parity import (FUSED_LENGTHS, FUSED_ROWS, MID_FUSED_ROWS, RAGGED_LENGTHS, RAGGED_ROWS, WIDE_FUSED_ROWS,
-                             custom_rows)
+from test_gpu_parity import (FUSED_LENGTHS, FUSED_ROWS, MID_FUSED_ROWS, RAGGED_LENGTHS, RAGGED_ROWS, TAIL_FUSED_LENGTHS,
+                             TAIL_FUSED_ROWS, WIDE_FUSED_ROWS, custom_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -125,7 +125,7 @@ def test_index_topk_fp8_equals_score_then_topk(k):
     # the fused FP8 pass (42 and 14 rows x 25 segments of 8192 columns) and the separate passes (2 rows)
     # against FP8 scores then top-K: bit-identical index sets
     for lengths, rows, seed in ((FUSED_LENGTHS, FP8_FUSED_ROWS, 44), (FUSED_LENGTHS, FUSED_ROWS, 50),
-                                (FUSED_LENGTHS, MID_FUSED_ROWS, 53),
+                                (FUSED_LENGTHS, MID_FUSED_ROWS, 53), (TAIL_FUSED_LENGTHS, TAIL_FUSED_ROWS, 55),
                                 ([20000, 9000], [(0, 19999), (1, 8999)], 45)):
         x = custom_rows(lengths, rows, attn=False, seed=seed)
         c = x["cfg"]

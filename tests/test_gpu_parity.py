@@ -529,6 +529,10 @@ FUSED_ROWS = [(b, L - 1) for b, L in enumerate(FUSED_LENGTHS)] + [(8, 9000), (9,
 WIDE_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 4001 * i) for i in range(1, 29)]
 # 24 rows x 13 chunks (312 blocks, one round): 16384-column chunks, one 8-wave block per CU
 MID_FUSED_ROWS = FUSED_ROWS + [(9, 200000 - 9001 * i) for i in range(1, 11)]
+# 60 rows x 19 chunks of 16384 columns (1140 blocks): more than two rounds of two 4-wave blocks per CU,
+# rows ending all along the sequence
+TAIL_FUSED_LENGTHS = FUSED_LENGTHS + [300000]
+TAIL_FUSED_ROWS = FUSED_ROWS + [(10, 299999 - 6001 * i) for i in range(46)]
 
 
 @pytest.mark.parametrize("distinct", [1, 3, 40, 4096])
@@ -589,7 +593,8 @@ def test_index_topk_equals_score_then_topk(k):
     # lsa_index_topk on the fused pass (14 rows x 25 segments of 8192 columns) and on the separate
     # passes (2 rows) against scoring everything and then selecting: bit-identical index sets
     for lengths, rows, seed in ((FUSED_LENGTHS, FUSED_ROWS, 42), (FUSED_LENGTHS, WIDE_FUSED_ROWS, 51),
-                                (FUSED_LENGTHS, MID_FUSED_ROWS, 52), ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
+                                (FUSED_LENGTHS, MID_FUSED_ROWS, 52), (TAIL_FUSED_LENGTHS, TAIL_FUSED_ROWS, 54),
+                                ([20000, 9000], [(0, 19999), (1, 8999)], 43)):
         x = custom_rows(lengths, rows, attn=False, seed=seed)
         c = x["cfg"]
         bud = (c["k_sink"], c["k_swa"], k)

@@ -430,10 +430,7 @@ constexpr int fused_lds_words(int C)
 }
 
 // Order key of a score for the selection (0: not a candidate).
-__device__ __attribute__((always_inline)) inline uint32_t select_key(float v)
-{
-    return is_candidate(v) ? float_order_key(v) : 0u;
-}
+__device__ __attribute__((always_inline)) inline uint32_t select_key(float v) { return candidate_key(v); }
 
 // v_mbcnt: the set bits of mask in the lanes below this one.
 __device__ __attribute__((always_inline)) inline uint32_t lanes_below(uint64_t mask)

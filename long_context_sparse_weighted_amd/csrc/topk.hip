@@ -84,10 +84,10 @@ __global__ __launch_bounds__(NT, SRC_SCORES && VPT == 32 ? kScoreLevelWavesPerEU
 #pragma unroll
             for (int q = 0; q < VPT / 4; ++q) {
                 const float4 v = src[q];
-                key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
-                key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
-                key[4 * q + 2] = is_candidate(v.z) ? float_order_key(v.z) : 0u;
-                key[4 * q + 3] = is_candidate(v.w) ? float_order_key(v.w) : 0u;
+                key[4 * q] = candidate_key(v.x);
+                key[4 * q + 1] = candidate_key(v.y);
+                key[4 * q + 2] = candidate_key(v.z);
+                key[4 * q + 3] = candidate_key(v.w);
             }
         } else if ((ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
             // A partial segment: whole float4 where it lies below n_in, single elements only in the
@@ -104,17 +104,17 @@ __global__ __launch_bounds__(NT, SRC_SCORES && VPT == 32 ? kScoreLevelWavesPerEU
                     v.y = c + 1 < n_in ? row[c + 1] : -INFINITY;
                     v.z = c + 2 < n_in ? row[c + 2] : -INFINITY;
                 }
-                key[4 * q] = is_candidate(v.x) ? float_order_key(v.x) : 0u;
-                key[4 * q + 1] = is_candidate(v.y) ? float_order_key(v.y) : 0u;
-                key[4 * q + 2] = is_candidate(v.z) ? float_order_key(v.z) : 0u;
-                key[4 * q + 3] = is_candidate(v.w) ? float_order_key(v.w) : 0u;
+                key[4 * q] = candidate_key(v.x);
+                key[4 * q + 1] = candidate_key(v.y);
+                key[4 * q + 2] = candidate_key(v.z);
+                key[4 * q + 3] = candidate_key(v.w);
             }
         } else {
 #pragma unroll
             for (int m = 0; m < VPT; ++m) {
                 const int64_t c = base + m;
                 const float v = c < n_in ? row[c] : -INFINITY;
-                key[m] = is_candidate(v) ? float_order_key(v) : 0u;
+                key[m] = candidate_key(v);
             }
         }
         if (page_row) {

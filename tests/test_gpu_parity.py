@@ -409,6 +409,26 @@ def test_attention_bf16_many_rows_single_split():
     assert_attn_close(host(out)[sel], want_o, host(lse)[sel], want_l, 2e-2)
 
 
+def test_attention_bf16_ragged_batch_192_rows():
+    # 192 rows of 128 heads (the ragged MTP batch's count: one block per row, more than half the CUs):
+    # rows of every list length, down to rows near the start of their sequence that hold almost no
+    # list (the positions repeat, each row with its own query and picks)
+    lengths = [3000, 6000, 700, 60]
+    base = [(0, 2999), (1, 5999), (1, 4000), (0, 1500), (2, 699), (2, 100), (3, 0), (3, 59), (1, 1039),
+            (1, 1040), (1, 2064), (0, 2200)]
+    rows = base * 16
+    x = custom_rows(lengths, rows, seed=9)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    idx = _oracle_idx_for(x, 1024, np.random.default_rng(6))
+    out, lse = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], budget_of(c),
+                                   torch.from_numpy(idx).to(DEV))
+    sel = np.concatenate([np.arange(12), np.arange(12, len(rows), 13)])
+    want_o, want_l = ref.hybrid_attn(o["kv_off"], o["row_seq"][sel], o["row_pos"][sel], o["q"][sel], o["kv"], 512,
+                                     c["scale"], 16, 1024, idx[sel])
+    log("192-row attn max err", assert_attn_close(host(out)[sel], want_o, host(lse)[sel], want_l, 2e-2))
+
+
 @pytest.mark.parametrize("repeat", [1, 40])
 def test_attention_bf16_late_dominant_logit(repeat):
     # Latent rows whose last 64 dims (outside the value part) align with head 0's query give that head a

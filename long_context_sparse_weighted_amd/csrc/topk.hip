@@ -6,10 +6,10 @@
 // segment of 16384 keys in registers (thread t holds positions 32 t .. 32 t + 31 of the segment; a
 // whole row of at most 4096 columns goes to one block of 256 threads x 16 keys, a final list of at
 // most 8192 candidates to 512 threads x 16) and picks its best k under (key desc, position asc) by
-// MSB-first radix select.  The bits the block's smallest and largest candidates share are fixed at
-// once (every candidate shares them); the rest are taken in digits of at most 11 bits, each counted
-// in an LDS histogram whose suffix sums locate the bin of the k-th key; keys above that bin are
-// picked and, once all 32 bits are fixed, ties take the lowest positions.
+// MSB-first radix select over the range its keys take: from [kmin, kmax], each pass splits the
+// interval holding the k-th key into 2^11 bins, counted in an LDS histogram whose suffix sums locate
+// the bin of the k-th key; keys above that bin are picked, and once the bin holds at most 64 keys one
+// wave ranks them exactly; ties at the k-th key's value take the lowest positions.
 // The picks are written in position order.  The first level cuts each row into segments of 16384
 // scores and writes every segment's picks as a candidate list (key, position): the row's top k is
 // among them, since an element with fewer than k better elements in its row has fewer than k

@@ -1,8 +1,8 @@
 // topk_block.hpp -- the block-level exact selection shared by the top-K levels (topk.hip) and the
 // fused scoring + first-level selection (index_score.hip): a block holds its keys in registers and
-// picks its best k under (key desc, position asc) by MSB-first radix select on LDS histograms, then
-// writes the picks to LDS in position order.  (Keys: order-preserving images of the scores, 0 = not a
-// candidate.)
+// picks its best k under (key desc, position asc) by radix select over the keys' own range on LDS
+// histograms, finished by a one-wave ranking, then writes the picks to LDS in position order.  (Keys:
+// order-preserving images of the scores, 0 = not a candidate.)
 #pragma once
 #include "lsa_dev.hpp"
 

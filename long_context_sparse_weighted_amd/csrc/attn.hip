@@ -830,18 +830,19 @@ constexpr int kMaxSplit = kMaxSplitMerge;
 
 // Splits of each row's selected list: the grid runs in rounds of 256 blocks (one per CU), a block costs
 // its tiles plus a fixed part (Q load, pick compaction, partial store: about 5 tiles' worth), so the
-// split count minimises rounds x (tiles per split + 5), with at least 4 tiles per split.
+// split count minimises rounds x (tiles per split + 5), with at least 2 tiles per split.
 static int pick_split(int n_rows, int n_heads, int k_total)
 {
     // Time model in units of one 32-row tile step of a block (about 2.4-3.2 us): a launch takes
     // rounds x (tiles per split + 5) units (5 for a block's fixed costs: q loads, pick compaction, the
     // first tile's latency, the output stores), and with ns > 1 the merge kernel adds its launch
     // (about 2.5 us) and its traffic (the bf16 partials read and the output written, at about
-    // 4.4 TB/s).  Measured: 8 rows take 13 splits, 32 rows 8, 64 rows 4; 192 rows (a ragged batch of
-    // drafts) run unsplit, where 4 splits cost 183 + 25 us of merge.
+    // 4.4 TB/s).  Measured: 8 rows take 22 splits of 3 tiles (29.0 us against 30.8 with 13 of 5; 33 of 2
+    // need a second round: 43 us), 32 rows 8, 64 rows 4; 192 rows (a ragged batch of drafts) run
+    // unsplit, where 4 splits cost 183 + 25 us of merge.
     const int64_t row_blocks = (int64_t)n_rows * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
     const int n_tiles = (k_total + kRowsPerTile - 1) / kRowsPerTile;
-    const int max_split = min(kMaxSplit, max(1, n_tiles / 4));
+    const int max_split = min(kMaxSplit, max(1, n_tiles / 2));
     constexpr double kUnitUs = 2.8;
     int best = 1;
     double best_cost = 1e300;

@@ -77,6 +77,9 @@ __device__ inline ColMap make_colmap(const RowInfo &ri, const SiRanges &g, const
             m.last_page = tp < n_pages - 1 ? tp : n_pages - 1;
         }
         m.G = P / B;
+        // the sub-blocks with a score, as a column range: those of the causal pages that exist
+        m.lo = 0;
+        m.hi = (m.last_page + 1) * m.G < m.nsb ? (m.last_page + 1) * m.G : m.nsb;
     }
     return m;
 }
@@ -148,147 +151,11 @@ __device__ inline int32_t group_seq(const RowsDev &rows, int grp)
     return valid == 0 ? -1 : __shfl(ri.seq, __ffsll((long long)valid) - 1, kWave);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void score_mfma_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
-                                                          const float *__restrict__ w,
-                                                          const uint16_t *__restrict__ keys, int k_sink, int k_swa,
-                                                          const int64_t *sb_off, const int32_t *pages, int M, int P,
-                                                          int B, float *__restrict__ scores, int64_t ld,
-                                                          int64_t n_cols, int64_t cols_per_block,
-                                                          const uint8_t *row_mode, int want, int grouped)
-{
-    const int r = blockIdx.y;
-    if (row_mode && row_mode[r] != want)
-        return;
-    if (grouped && group_uniform(rows, row_mode, want, r / kGroupRows))
-        return;  // scored by the multi-row kernel
-    const RowInfo ri = row_info(rows, r);
-    const SiRanges si = si_ranges(ri, k_sink, k_swa);
-    const ColMap cm = make_colmap<MODE>(ri, si, sb_off, pages, r, M, P, B);
-
-    const int lane = lane_id();
-    const int n = lane & 15;  // key column within the tile / head row within an MFMA tile
-    const int g = lane >> 4;  // lane group: depth 32ks + 8g .. +8 of step ks; heads 4g..4g+3 of each tile
-    const int wave = threadIdx.x >> 6;
-
-    const int64_t c_begin = (int64_t)blockIdx.x * cols_per_block;
-    int64_t c_end = c_begin + cols_per_block;
-    if (c_end > n_cols)
-        c_end = n_cols;
-    float *out = scores + (int64_t)r * ld;
-
-    // A operands: q rows of this query, head mt*16 + n, depth 32ks + 8g .. +8.
-    u32x4 qa[4][4];
-    const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qa[mt][ks] = src[4 * ks];
-    }
-    // Head weights of the 16 heads whose dot products this lane ends up holding.
-    float wv[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wv[mt][i] = v[i];
-    }
-
-    const int64_t first_tile = c_begin / kTile + wave;
-    const int64_t end_tile = (c_end + kTile - 1) / kTile;
-
-    // A row with nothing to score writes -inf over its columns and issues no loads.
-    const bool row_has_keys = MODE == kModePageMean ? cm.nsb > 0 : cm.lo < cm.hi;
-    if (!row_has_keys) {
-        if (MODE == kModePageMean) {
-            for (int64_t p = c_begin / cm.G + threadIdx.x; p < (c_end + cm.G - 1) / cm.G && p < ld; p += blockDim.x)
-                out[p] = -INFINITY;
-        } else {
-            for (int64_t c = c_begin + threadIdx.x; c < c_end; c += blockDim.x)
-                out[c] = -INFINITY;
-        }
-        return;
-    }
-    // Columns without a score still load a row of the sequence (its first scored key), so every
-    // load is unconditional and the loads of later tiles stay in flight across iterations.
-    const int64_t safe_key = MODE == kModePageMean ? cm.base : cm.base + cm.lo;
-    auto load_tile = [&](int64_t tile, u32x4 (&b)[4], int64_t &key) {
-        key = col_key<MODE>(cm, tile * kTile + n);
-        const int64_t row_k = key >= 0 ? key : safe_key;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(keys + row_k * kDim + g * 8);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            b[ks] = src[4 * ks];
-    };
-
-    // One tile: MFMAs, ReLU + head weights, reduction over the 4 lane groups, store.
-    auto compute = [&](int64_t tile, const u32x4 (&b)[4], int64_t key) {
-        const bool any = __ballot(key >= 0) != 0;  // wave-uniform
-        float v = 0.0f;
-        if (any) {
-            f32x4 acc[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb,
-                                                                      acc[mt], 0, 0, 0);
-            }
-            // acc[mt][i] = q(head mt*16 + 4g + i) . k(column n)
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v += wv[mt][i] * relu(acc[mt][i]);
-            v = sum_xor32(sum_xor16(v));
-        }
-        const int64_t c = tile * kTile + n;
-        if (MODE == kModePageMean) {
-            // Sum the G sub-blocks of each page (they are G consecutive columns of this tile); a
-            // sub-block that does not exist adds nothing.
-            if (key < 0)
-                v = 0.0f;
-            for (int o = 1; o < cm.G; o <<= 1)
-                v += __shfl_xor(v, o, kWave);
-            // (every lane group holds the same sums; all of them store, without branching)
-            const int64_t p = c / cm.G;
-            if ((n % cm.G) == 0 && p < ld)
-                out[p] = (p <= cm.last_page) ? v : -INFINITY;
-        } else if (c < c_end) {
-            out[c] = key >= 0 ? v : -INFINITY;
-        }
-    };
-
-    // Three register buffers: two tiles are in flight while the third is multiplied.
-    constexpr int64_t W = kWavesPerBlock;
-    u32x4 b0[4], b1[4], b2[4];
-    int64_t k0 = -1, k1 = -1, k2 = -1;
-    int64_t tile = first_tile;
-    load_tile(tile, b0, k0);
-    load_tile(tile + W, b1, k1);
-    for (; tile < end_tile; tile += 3 * W) {
-        load_tile(tile + 2 * W, b2, k2);
-        compute(tile, b0, k0);
-        load_tile(tile + 3 * W, b0, k0);
-        if (tile + W < end_tile)
-            compute(tile + W, b1, k1);
-        load_tile(tile + 4 * W, b1, k1);
-        if (tile + 2 * W < end_tile)
-            compute(tile + 2 * W, b2, k2);
-    }
-}
-
 // ------------------------------------------------------------------------------------------
-// Streaming bf16 kernel (decode): the same per-row work as score_mfma_kernel, with the keys moved by
-// LDS DMA.  A DMA instruction reads 1 KB of whole 128-byte lines (4 key rows), where an MFMA operand
-// load reads 64 bytes of each of 16 rows.  Each wave streams its own tiles through a private ring
+// Streaming bf16 kernel (rows scored one by one: decode, and page-mean rows of HI stage 1): a row's q
+// (64 heads x 128 dims) stays in VGPRs as the A operands of v_mfma_f32_16x16x32_bf16 and the keys (or
+// sub-block means) stream past it, moved by LDS DMA.  A DMA instruction reads 1 KB of whole 128-byte
+// lines (4 key rows), where an MFMA operand load reads 64 bytes of each of 16 rows.  Each wave streams its own tiles through a private ring
 // of S 4 KB buffers (up to S tiles in flight), so no barrier is needed.  Chunk c of key k of a tile
 // sits at slot 16 k + (c ^ k): the 16 lanes reading one operand hit 16 different bank groups.
 //
@@ -391,7 +258,7 @@ __device__ inline void chunk_key_range(const ColMap &cm, int64_t c_first, int64_
 {
     c_begin = c_first;
     c_end = c_last;
-    if constexpr (MODE == kModeFlat) {
+    if constexpr (MODE == kModeFlat || MODE == kModePageMean) {
         c_begin = max(c_first, cm.lo / 64 * 64);
         c_end = min(c_last, cm.hi);
     } else {
@@ -542,6 +409,7 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ keys, int k_sink, int k_swa,
                                                             const int32_t *__restrict__ pages, int M, int P,
+                                                            const int64_t *__restrict__ sb_off, int B,
                                                             float *__restrict__ scores, int64_t ld, int64_t n_cols,
                                                             int64_t cols_per_block, const uint8_t *row_mode, int want,
                                                             int grouped, int k_sel, uint32_t *__restrict__ sel_key,
@@ -580,7 +448,7 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
     __shared__ __attribute__((aligned(16))) uint16_t ring[S][WV][kTile * kDim];
     const RowInfo ri = row_info(rows, r);
     const SiRanges si = si_ranges(ri, k_sink, k_swa);
-    const ColMap cm = make_colmap<MODE>(ri, si, nullptr, pages, r, M, P, 1);
+    const ColMap cm = make_colmap<MODE>(ri, si, sb_off, pages, r, M, P, B);
 
     const int lane = lane_id();
     const int n = lane & 15;
@@ -599,7 +467,19 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
     int64_t c_begin, c_end;
     chunk_key_range<MODE>(cm, c_first, c_last, c_begin, c_end);
     const bool empty = cm.lo >= cm.hi || c_begin >= c_end;  // no keys here (the DMAs need a row of keys)
-    if constexpr (!SELECT) {
+    if constexpr (MODE == kModePageMean) {
+        // Page-mean columns are sub-blocks and the output holds one score per page of G of them (chunks
+        // start on whole pages): the pages with no sub-block in [c_begin, c_end) are -inf.
+        const int64_t G = cm.G;
+        const int64_t p_end = (c_last + G - 1) / G < ld ? (c_last + G - 1) / G : ld;
+        const int64_t p_lo = empty ? p_end : c_begin / G, p_hi = empty ? p_end : (c_end + G - 1) / G;
+        for (int64_t p = c_first / G + threadIdx.x; p < p_lo; p += blockDim.x)
+            out[p] = -INFINITY;
+        for (int64_t p = p_hi + threadIdx.x; p < p_end; p += blockDim.x)
+            out[p] = -INFINITY;
+        if (empty)
+            return;
+    } else if constexpr (!SELECT) {
         if (empty) {
             for (int64_t c = c_first + threadIdx.x; c < c_last; c += blockDim.x)
                 out[c] = -INFINITY;
@@ -667,7 +547,7 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
         // one page (P is a multiple of 16), so the page table is read once per tile, by a scalar load.
         auto tile_pos = [&](int64_t tile) __attribute__((always_inline)) -> int64_t {
             const int64_t c0 = tile * kTile;
-            if constexpr (MODE == kModeFlat) {
+            if constexpr (MODE != kModePaged) {
                 return c0;
             } else {
                 // (columns and slots fit in 32 bits; readfirstlane keeps the index in scalar registers)
@@ -793,8 +673,19 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
                 for (int64_t k0 = 0; k0 < K; k0 += 4) {
                     int64_t c;
                     const float v = group(k0, c);
-                    if (c < c_end)
+                    if constexpr (MODE == kModePageMean) {
+                        // the G sub-blocks of a page are G consecutive lanes of a lane group: their scores
+                        // are summed (a sub-block that does not exist adds nothing) and the page's first
+                        // lane stores the page score, -inf past the row's last causal page
+                        float pv = v == -INFINITY ? 0.0f : v;
+                        for (int o = 1; o < cm.G; o <<= 1)
+                            pv += __shfl_xor(pv, o, kWave);
+                        const int64_t pg = c / cm.G;
+                        if (c < c_end && (n & (cm.G - 1)) == 0 && pg < ld)
+                            out[pg] = pg <= cm.last_page ? pv : -INFINITY;
+                    } else if (c < c_end) {
                         out[c] = v;
+                    }
                 }
             }
             wait_vmcnt<0>();  // the ring's trailing DMA writes land before the block's LDS is reused
@@ -1490,10 +1381,14 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
         if (all_grouped) {
             // (nothing left for the per-row kernels)
         } else if constexpr (MODE == kModePageMean) {
-            dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
-            hipLaunchKernelGGL(score_mfma_kernel<MODE>, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
-                               (const uint16_t *)keys, k_sink, k_swa, sb_off, pages, M, P, B, scores, ld, n_cols,
-                               geo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0);
+            // rows scored one by one stream the means through LDS like the flat rows (chunks of whole
+            // 64-column groups, so of whole pages)
+            const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
+            dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
+            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
+                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, nullptr, 0, P, sb_off,
+                               B, scores, ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0,
+                               nullptr, nullptr, 0, grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
         } else {
             ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             if (MODE == kModePaged && (rows.n_rows < kMinGroupedRows || rows.n_rows < kGroupRows * rows.n_seq) &&
@@ -1504,8 +1399,8 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
             }
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
             hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
-                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, scores,
-                               ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
+                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, nullptr,
+                               1, scores, ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
                                nullptr, 0, grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
         }
     } else {
@@ -1644,17 +1539,17 @@ hipError_t launch_index_select_fused(const RowsDev &rows, const void *q_idx, con
     if (cols == 2 * kFusedCols && (int64_t)grid.x * grid.y >= 512)  // two blocks of 4 waves per CU
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, 2 * kFusedCols>), grid, dim3(256), 0, stream,
                            rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1,
-                           nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld,
+                           nullptr, 1, nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos, sel_ld,
                            gate.list, gate.count, gate.table, gate.table_count);
     else if (cols == 2 * kFusedCols)  // one round of blocks: one block of 8 waves per CU
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing8, 2 * kFusedCols, 8>), grid, dim3(512), 0,
                            stream, rows, (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0,
-                           1, nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
+                           1, nullptr, 1, nullptr, (int64_t)0, n_cols, cols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
                            sel_ld, gate.list, gate.count, gate.table, gate.table_count);
     else
         hipLaunchKernelGGL((score_stream_kernel<kModeFlat, kFusedRing, kFusedCols>), grid, dim3(256), 0, stream, rows,
                            (const uint16_t *)q_idx, w, (const uint16_t *)k_idx, k_sink, k_swa, nullptr, 0, 1, nullptr,
-                           (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
+                           1, nullptr, (int64_t)0, n_cols, (int64_t)kFusedCols, gate.row_mode, gate.want, 0, k, sel_key, sel_pos,
                            sel_ld, gate.list, gate.count, gate.table, gate.table_count);
     return hipGetLastError();
 }

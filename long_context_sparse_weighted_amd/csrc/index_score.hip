@@ -627,18 +627,17 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
     #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         v += wv[mt][i] * relu(acc[mt][i]);
-                v = sum_xor32(sum_xor16(v));
             }
-            return v;
+            return v;  // this lane group's part (its 16 heads) of key n's score
         };
         // Group k0 / 4 (tiles k0 .. k0 + 3): lane group g takes tile g's 16 scores (-inf past c_end or
-        // where a column holds no key).
+        // where a column holds no key), the four tiles' partial scores folded by lane swaps.
         auto group = [&](int64_t k0, int64_t &c) __attribute__((always_inline)) -> float {
             const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
             const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
             const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
             const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-            const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+            const float v = sum_halves_swap32(sum_rows_swap16(v0, v1), sum_rows_swap16(v2, v3));
             const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
             c = tile_of(k0 + g) * kTile + n;
             return c < c_end && key_of(tp, n) >= 0 ? v : -INFINITY;
@@ -984,17 +983,21 @@ LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 8)
 //
 // Block = 16 waves, one row each (its 64x128 query block in VGPRs): four waves per SIMD at 128
 // registers, so one wave's ReLU / weight epilogue runs beside another's matrix products.  Keys arrive
-// in stages of 128 (32 KB) by LDS DMA, double-buffered, one barrier per stage.  Inside a stage the
-// 16-byte chunk c of key k is stored at slot 16 k + (c ^ (k % 16)), so the 16 lanes that read one
-// MFMA operand hit 16 different bank groups.  Four tiles are scored before their results are stored:
-// lane group g stores tile g, so one store instruction writes 256 contiguous bytes.
+// in stages of 256 (64 KB) by LDS DMA, double-buffered, one barrier per stage (256 rather than 128
+// keys: half the barriers, 1 % faster).  Inside a stage the 16-byte chunk c of key k is stored at slot
+// 16 k + (c ^ (k % 16)), so the 16 lanes that read one MFMA operand hit 16 different bank groups.  Four
+// tiles are scored before their results are stored: lane group g stores tile g, so one store
+// instruction writes 256 contiguous bytes.  Each lane group holds a partial score (its 16 heads) of each
+// tile; the four partials are folded by two lane swaps of row pairs and one of halves (six instructions
+// for four tiles instead of a full four-step reduction per tile and a select: the epilogue's vector
+// instructions share the issue port with the products, 3 % faster).
 
 constexpr int kGroupWaves = 16;
 constexpr int kGroupThreads = kGroupWaves * kWave;
-constexpr int kStageKeys = 128;
-constexpr int kStageTiles = kStageKeys / kTile;              // 8
-constexpr int kStageElems = kStageKeys * kDim;               // bf16 elements per stage (32 KB)
-constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 32 wave-wide 1 KB DMA writes
+constexpr int kStageKeys = 256;
+constexpr int kStageTiles = kStageKeys / kTile;              // 16
+constexpr int kStageElems = kStageKeys * kDim;               // bf16 elements per stage (64 KB)
+constexpr int kStageDma = kStageElems * 2 / (16 * kWave);    // 64 wave-wide 1 KB DMA writes
 constexpr int kMinGroupedRows = 64;                          // fewer rows: the per-row kernel only
 static_assert(kGroupWaves == kGroupRows, "one row per wave");
 
@@ -1098,7 +1101,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
             }
         }
         // DMA j = wave + 16 jj of a stage fills slots 64 j .. 64 j + 63, i.e. keys 4 j .. 4 j + 3: this
-        // lane moves chunk c16 of key 4 wave + 64 jj + g (the same chunk for both jj).
+        // lane moves chunk c16 of key 4 wave + 64 jj + g (the same chunk for every jj).
         const int kk0 = 4 * wave + g;
         const int c16 = n ^ (kk0 & 15);
         const uint16_t *kseq = keys + base * kDim;
@@ -1142,7 +1145,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     v += wv[mt][i] * relu(acc[mt][i]);
-            return sum_xor32(sum_xor16(v));
+            return v;
         };
 
         // One stage: wait for its DMA, start the next stage's into the other buffer, score 8 tiles.
@@ -1159,12 +1162,20 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
 #pragma unroll 1
             for (int t4 = 0; t4 < kStageTiles; t4 += 4) {
                 // one tile at a time (four in flight would not fit in 128 registers)
-                float v = 0.0f;
+                // partial scores of tiles t4 .. t4 + 3 (each lane group holds its 16 heads' part), folded
+                // pairwise: lane group g ends with the whole score of tile t4 + g
+                float ya = 0.0f, yb = 0.0f;
 #pragma unroll 1
-                for (int q = 0; q < 4; ++q) {
-                    const float vq = score_tile(buf, t4 + q);
-                    v = g == q ? vq : v;
+                for (int h = 0; h < 2; ++h) {
+                    int tt = t4 + 2 * h;
+                    const float p0 = score_tile(buf, tt);
+                    // the next tile's operand reads wait for this score (one tile in flight)
+                    asm volatile("" : "+s"(tt) : "v"(p0));
+                    const float p1 = score_tile(buf, tt + 1);
+                    yb = sum_rows_swap16(p0, p1);
+                    ya = h == 0 ? yb : ya;
                 }
+                const float v = sum_halves_swap32(ya, yb);
                 const int rel = (t4 + g) * kTile + n;
                 if constexpr (MODE == kModePageMean) {
                     float pv = col0 + rel < n_keys ? v : 0.0f;

@@ -201,14 +201,24 @@ __device__ inline float sum_xor16(float v)
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
+// Lane swaps for folding per-lane-group partials (lane group g = lane / 16).  sum_rows_swap16(a, b):
+// groups 0 and 2 get a summed over their group pair (0+1, 2+3), groups 1 and 3 get b summed likewise.
+// sum_halves_swap32(a, b): the lower half (groups 0, 1) gets a summed over the two halves, the upper
+// half b.  So sum_halves_swap32(sum_rows_swap16(p0, p1), sum_rows_swap16(p2, p3)) leaves group g with
+// p_g summed over all four groups.
+__device__ inline float sum_rows_swap16(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ inline float sum_halves_swap32(float a, float b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 __device__ inline float max_xor32(float v)
 {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ inline float max_xor16(float v)
-{
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 

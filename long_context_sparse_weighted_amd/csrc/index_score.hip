@@ -637,7 +637,7 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
             const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
             const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
             const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-            const float v = sum_halves_swap32(sum_rows_swap16(v0, v1), sum_rows_swap16(v2, v3));
+            const float v = sum_halves32(sum_rows_swap16(v0, v1), sum_rows_swap16(v2, v3));
             const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
             c = tile_of(k0 + g) * kTile + n;
             return c < c_end && key_of(tp, n) >= 0 ? v : -INFINITY;
@@ -884,11 +884,12 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
             dma_4(k_scale + (key >= 0 ? key : safe_key), buf + kTileCodes8);
         }
     };
-    auto score_tile = [&](int64_t k, int64_t tp) __attribute__((always_inline)) -> float {
+    // this lane group's part (its 16 heads) of key n's unscaled score; sk = the key's scale
+    auto score_tile = [&](int64_t k, int64_t tp, float &sk) __attribute__((always_inline)) -> float {
         wait_vmcnt<3 * (S - 1)>();  // DMA(k) has landed: only DMA(k + 1 .. k + S - 1) may follow it
         const bool any = interior(tp) || __ballot(key_of(tp, n) >= 0) != 0;  // wave-uniform
         u32x4 b0 = u32x4{0u, 0u, 0u, 0u}, b1 = b0;
-        float sk = 0.0f;
+        sk = 0.0f;
         if (any) {
             const uint8_t *slot = &ring[k % S][wave][0];
             const int f = (n >> 1) & 7;
@@ -913,18 +914,19 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     v += wv[mt][i] * relu(acc[mt][i]);
-            v = sum_xor32(sum_xor16(v)) * sk;
         }
         return v;
     };
     // Group k0 / 4 (tiles k0 .. k0 + 3): lane group g takes tile g's 16 scores (-inf past c_end or
-    // where a column holds no key).
+    // where a column holds no key), the four tiles' partial sums folded by lane swaps, then scaled.
     auto group = [&](int64_t k0, int64_t &c) __attribute__((always_inline)) -> float {
         const int64_t tp0 = tile_pos(tile_of(k0)), tp1 = tile_pos(tile_of(k0 + 1));
         const int64_t tp2 = tile_pos(tile_of(k0 + 2)), tp3 = tile_pos(tile_of(k0 + 3));
-        const float v0 = score_tile(k0, tp0), v1 = score_tile(k0 + 1, tp1);
-        const float v2 = score_tile(k0 + 2, tp2), v3 = score_tile(k0 + 3, tp3);
-        const float v = g == 0 ? v0 : g == 1 ? v1 : g == 2 ? v2 : v3;
+        float s0, s1, s2, s3;
+        const float v0 = score_tile(k0, tp0, s0), v1 = score_tile(k0 + 1, tp1, s1);
+        const float v2 = score_tile(k0 + 2, tp2, s2), v3 = score_tile(k0 + 3, tp3, s3);
+        const float sk = g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
+        const float v = sum_halves32(sum_rows_swap16(v0, v1), sum_rows_swap16(v2, v3)) * sk;
         const int64_t tp = g == 0 ? tp0 : g == 1 ? tp1 : g == 2 ? tp2 : tp3;
         c = tile_of(k0 + g) * kTile + n;
         return c < c_end && key_of(tp, n) >= 0 ? v : -INFINITY;
@@ -1175,7 +1177,7 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
                     yb = sum_rows_swap16(p0, p1);
                     ya = h == 0 ? yb : ya;
                 }
-                const float v = sum_halves_swap32(ya, yb);
+                const float v = sum_halves32(ya, yb);
                 const int rel = (t4 + g) * kTile + n;
                 if constexpr (MODE == kModePageMean) {
                     float pv = col0 + rel < n_keys ? v : 0.0f;

@@ -188,6 +188,12 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v)
     return v;
 }
 
+// Lane swaps over lane groups (lane group g = lane / 16).  sum_halves32(a, b): the lower half (groups 0
+// and 1) gets a summed over the two 32-lane halves, the upper half gets b summed likewise.
+// sum_rows_swap16(a, b): groups 0 and 2 get a summed over their group pair (0+1, 2+3), groups 1 and 3 get
+// b (permlane16_swap exchanges the odd 16-lane rows of its first operand with the even rows of its
+// second).  So sum_halves32(sum_rows_swap16(p0, p1), sum_rows_swap16(p2, p3)) leaves group g with p_g
+// summed over all four groups: six instructions fold four partials.
 __device__ inline float sum_halves32(float a, float b)
 {
     const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
@@ -195,25 +201,9 @@ __device__ inline float sum_halves32(float a, float b)
 }
 // Every lane: v[l] + v[l ^ 32].
 __device__ inline float sum_xor32(float v) { return sum_halves32(v, v); }
-// Every lane: v[l] + v[l ^ 16] (permlane16_swap exchanges odd 16-lane rows of a with even rows of b).
-__device__ inline float sum_xor16(float v)
-{
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-// Lane swaps for folding per-lane-group partials (lane group g = lane / 16).  sum_rows_swap16(a, b):
-// groups 0 and 2 get a summed over their group pair (0+1, 2+3), groups 1 and 3 get b summed likewise.
-// sum_halves_swap32(a, b): the lower half (groups 0, 1) gets a summed over the two halves, the upper
-// half b.  So sum_halves_swap32(sum_rows_swap16(p0, p1), sum_rows_swap16(p2, p3)) leaves group g with
-// p_g summed over all four groups.
 __device__ inline float sum_rows_swap16(float a, float b)
 {
     const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-__device__ inline float sum_halves_swap32(float a, float b)
-{
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 __device__ inline float max_xor32(float v)

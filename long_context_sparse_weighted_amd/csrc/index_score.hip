@@ -178,24 +178,38 @@ __device__ inline int32_t group_seq(const RowsDev &rows, int grp)
 constexpr int kScoreRing = LSA_SCORE_RING;
 
 // 16 bytes per lane from global memory to LDS at lds_base + 16 * lane (lds_base wave-uniform).
-// Cache policy of the key stream: each key is read once, as whole lines (sc0 nt: streaming).
-#ifndef LSA_DMA_CPOL
-#define LSA_DMA_CPOL "sc0 nt"
-#endif
+// Cache policy of a key stream (STREAM): a row reads each key once, as whole lines, so the DMA is marked
+// streaming (sc0 nt) and does not displace cached data -- unless other rows of the launch read the same
+// keys: paged and page-mean rows of one sequence (the pages several rows of a prefill chunk recall, the
+// means every row of a sequence scores) keep the default policy, under which those re-reads hit L2 and
+// the last-level cache (kernels' KEEP; HI stage 2 of a 2048-row prefill chunk at 1M: 11.2 -> 8.0 ms).
+// Rows that share nothing stream (flat decode under the default policy: 8 % slower; HI decode of 8
+// sequences with B = 8: 10 % slower).
+template <bool STREAM>
 __device__ inline void dma_16(const void *src, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " LSA_DMA_CPOL ::"v"(src),
-                 "s"(lds_base)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off sc0 nt" ::"v"(src),
+                     "s"(lds_base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+                     : "memory", "m0");
 }
 
 // The same from a wave-uniform base (SGPR pair) plus a per-lane 32-bit byte offset: no per-lane
 // 64-bit address arithmetic.  (The kernels using these do not otherwise use M0.)
+template <bool STREAM>
 __device__ inline void dma_16s(const void *sbase, uint32_t voff, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 " LSA_DMA_CPOL ::"v"(voff),
-                 "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 sc0 nt" ::"v"(voff),
+                     "s"(sbase), "s"(lds_base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+                     "s"(lds_base)
+                     : "memory", "m0");
 }
 
 template <int N>
@@ -404,7 +418,7 @@ __device__ inline void fused_select_regs(const uint32_t (&key)[C / NT], KeyStats
     }
 }
 
-template <int MODE, int S, int SEL, int WV = kWavesPerBlock>
+template <int MODE, int S, int SEL, int WV = kWavesPerBlock, bool KEEP = false>
 __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, const uint16_t *__restrict__ q_idx,
                                                             const float *__restrict__ w,
                                                             const uint16_t *__restrict__ keys, int k_sink, int k_swa,
@@ -581,14 +595,14 @@ __global__ __launch_bounds__(64 * WV) void score_stream_kernel(RowsDev rows, con
                 const uint16_t *kb = keys + (cm.base + tp) * kDim;
     #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    dma_16s(kb, lane_off[j], buf + j * 1024);
+                    dma_16s<!KEEP>(kb, lane_off[j], buf + j * 1024);
             } else {
     #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int kk = 4 * j + g;
                     const int64_t key = key_of(tp, kk);
                     const int64_t row_k = key >= 0 ? key : safe_key;
-                    dma_16(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
+                    dma_16<!KEEP>(keys + row_k * kDim + (n ^ kk) * 8, buf + j * 1024);
                 }
             }
         };
@@ -726,20 +740,32 @@ constexpr int kDim8 = 128;                          // bytes per key (E4M3 codes
 constexpr int kTileCodes8 = kTile * kDim8;          // 2 KB
 constexpr int kSlot8 = kTileCodes8 + 64 * 4;        // + the scale copies
 
+// 4 bytes per lane (the key scales), with the cache policy of the key stream they belong to.
+template <bool STREAM>
 __device__ inline void dma_4s(const void *sbase, uint32_t voff, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 " LSA_DMA_CPOL ::"v"(voff),
-                 "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 sc0 nt" ::"v"(voff), "s"(sbase),
+                     "s"(lds_base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+                     "s"(lds_base)
+                     : "memory", "m0");
 }
+template <bool STREAM>
 __device__ inline void dma_4(const void *src, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off " LSA_DMA_CPOL ::"v"(src),
-                 "s"(lds_base)
-                 : "memory", "m0");
+    if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off sc0 nt" ::"v"(src),
+                     "s"(lds_base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base)
+                     : "memory", "m0");
 }
 
-template <int MODE, int S, int SEL, int WV = kWavesPerBlock>
+template <int MODE, int S, int SEL, int WV = kWavesPerBlock, bool KEEP = false>
 __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const uint8_t *__restrict__ q8,
                                                          const float *__restrict__ q_scale,
                                                          const float *__restrict__ w, const uint8_t *__restrict__ k8,
@@ -870,18 +896,18 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
             const uint8_t *kb = k8 + (cm.base + tp) * kDim8;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                dma_16s(kb, lane_off[j], buf + j * 1024);
-            dma_4s(k_scale + cm.base + tp, scale_off, buf + kTileCodes8);
+                dma_16s<!KEEP>(kb, lane_off[j], buf + j * 1024);
+            dma_4s<!KEEP>(k_scale + cm.base + tp, scale_off, buf + kTileCodes8);
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int kk = 8 * j + (lane >> 3);
                 const int64_t key = key_of(tp, kk);
                 const int64_t row_k = key >= 0 ? key : safe_key;
-                dma_16(k8 + row_k * kDim8 + (((lane & 7) ^ ((kk >> 1) & 7)) * 16), buf + j * 1024);
+                dma_16<!KEEP>(k8 + row_k * kDim8 + (((lane & 7) ^ ((kk >> 1) & 7)) * 16), buf + j * 1024);
             }
             const int64_t key = key_of(tp, n);
-            dma_4(k_scale + (key >= 0 ? key : safe_key), buf + kTileCodes8);
+            dma_4<!KEEP>(k_scale + (key >= 0 ? key : safe_key), buf + kTileCodes8);
         }
     };
     // this lane group's part (its 16 heads) of key n's unscaled score; sk = the key's scale
@@ -968,15 +994,16 @@ __global__ __launch_bounds__(64 * WV) void score_fp8_kernel(RowsDev rows, const 
 }
 
 // (explicit instantiations: without them the host stub of the flat kernel is not emitted)
-#define LSA_FP8_INSTANCE(MODE, RING, SEL, WV)                                                                       \
-    template __global__ void score_fp8_kernel<MODE, RING, SEL, WV>(                                                    \
+#define LSA_FP8_INSTANCE(MODE, RING, SEL, WV, KEEP)                                                                 \
+    template __global__ void score_fp8_kernel<MODE, RING, SEL, WV, KEEP>(                                              \
         RowsDev, const uint8_t *, const float *, const float *, const uint8_t *, const float *, int, int,             \
         const int32_t *, int, int, float *, int64_t, int64_t, int64_t, int, uint32_t *, int32_t *, int64_t);
-LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, 0, 4)
-LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0, 4)
-LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, kFusedCols, 4)
-LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 4)
-LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 8)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, 0, 4, false)
+LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0, 4, false)
+LSA_FP8_INSTANCE(kModePaged, kFp8Ring, 0, 4, true)
+LSA_FP8_INSTANCE(kModeFlat, kFp8Ring, kFusedCols, 4, false)
+LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 4, false)
+LSA_FP8_INSTANCE(kModeFlat, kFp8WideRing, 2 * kFusedCols, 8, false)
 #undef LSA_FP8_INSTANCE
 
 // ------------------------------------------------------------------------------------------
@@ -1352,6 +1379,13 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
     return n_heads >= 1 && n_heads <= kHeads && (head_dim == 64 || head_dim == 128);
 }
 
+// Rows of one launch that read the same keys or means: at least two rows per sequence on average (a
+// prefill chunk), so the paged and page-mean streams keep the default cache policy.
+static bool rows_share_keys(const RowsDev &rows)
+{
+    return (int64_t)rows.n_rows >= 2 * (int64_t)rows.n_seq;
+}
+
 // Columns per block of the bf16 kernels: about one block per CU (256 CUs), at most 16384 columns.
 struct ScoreGeom {
     int64_t chunk_elems;
@@ -1398,10 +1432,12 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
             // 64-column groups, so of whole pages)
             const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
-            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
-                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, nullptr, 0, P, sb_off,
-                               B, scores, ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0,
-                               nullptr, nullptr, 0, grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
+            auto kernel = rows_share_keys(rows) ? score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, true>
+                                                : score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, false>;
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
+                               (const uint16_t *)keys, k_sink, k_swa, nullptr, 0, P, sb_off, B, scores, ld, n_cols,
+                               sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr, nullptr, 0,
+                               grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
         } else {
             ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             if (MODE == kModePaged && (rows.n_rows < kMinGroupedRows || rows.n_rows < kGroupRows * rows.n_seq) &&
@@ -1411,10 +1447,15 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
                 sgeo = ScoreGeom{2048, (int)((n_cols + 2047) / 2048)};
             }
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
-            hipLaunchKernelGGL((score_stream_kernel<MODE, kScoreRing, 0>), grid, dim3(256), 0, stream, rows,
-                               (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, P, nullptr,
-                               1, scores, ld, n_cols, sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr,
-                               nullptr, 0, grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
+            auto kernel = score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, false>;
+            if constexpr (MODE == kModePaged) {
+                if (rows_share_keys(rows))
+                    kernel = score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, true>;
+            }
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
+                               (const uint16_t *)keys, k_sink, k_swa, pages, M, P, nullptr, 1, scores, ld, n_cols,
+                               sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr, nullptr, 0,
+                               grouped ? nullptr : gate.list, gate.count, nullptr, nullptr);
         }
     } else {
         int64_t threads_cols = MODE == kModePageMean ? ld : n_cols;
@@ -1463,11 +1504,12 @@ hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const 
         return hipSuccess;
     const ScoreGeom geo = score_geometry(rows.n_rows, ld, LSA_FP8_BLOCKS_PER_CU);
     dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
-    if (pages)
-        hipLaunchKernelGGL((score_fp8_kernel<kModePaged, kFp8Ring, 0>), grid, dim3(256), 0, stream, rows, q8,
-                           q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
-                           nullptr, nullptr, (int64_t)0);
-    else
+    if (pages) {
+        auto kernel = rows_share_keys(rows) ? score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, true>
+                                            : score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, false>;
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, q8, q_scale, w, k8, k_scale, k_sink, k_swa, pages,
+                           M, P, scores, ld, ld, geo.chunk_elems, 0, nullptr, nullptr, (int64_t)0);
+    } else
         hipLaunchKernelGGL((score_fp8_kernel<kModeFlat, kFp8Ring, 0>), grid, dim3(256), 0, stream, rows, q8,
                            q_scale, w, k8, k_scale, k_sink, k_swa, pages, M, P, scores, ld, ld, geo.chunk_elems, 0,
                            nullptr, nullptr, (int64_t)0);

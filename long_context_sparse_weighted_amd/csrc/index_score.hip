@@ -1380,10 +1380,11 @@ bool index_score_supported(int dtype, int n_heads, int head_dim)
 }
 
 // Rows of one launch that read the same keys or means: at least two rows per sequence on average (a
-// prefill chunk), so the paged and page-mean streams keep the default cache policy.
-static bool rows_share_keys(const RowsDev &rows)
+// prefill chunk), so the paged and page-mean streams keep the default cache policy.  Under a row gate
+// only some rows run (the index owners of an MTP batch: one per sequence), so the streams stay streaming.
+static bool rows_share_keys(const RowsDev &rows, const RowGate &gate)
 {
-    return (int64_t)rows.n_rows >= 2 * (int64_t)rows.n_seq;
+    return gate.row_mode == nullptr && (int64_t)rows.n_rows >= 2 * (int64_t)rows.n_seq;
 }
 
 // Columns per block of the bf16 kernels: about one block per CU (256 CUs), at most 16384 columns.
@@ -1432,8 +1433,8 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
             // 64-column groups, so of whole pages)
             const ScoreGeom sgeo = score_geometry(rows.n_rows, n_cols, LSA_SCORE_BLOCKS_PER_CU);
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
-            auto kernel = rows_share_keys(rows) ? score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, true>
-                                                : score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, false>;
+            auto kernel = rows_share_keys(rows, gate) ? score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, true>
+                                                      : score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, false>;
             hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
                                (const uint16_t *)keys, k_sink, k_swa, nullptr, 0, P, sb_off, B, scores, ld, n_cols,
                                sgeo.chunk_elems, gate.row_mode, gate.want, grouped ? 1 : 0, 0, nullptr, nullptr, 0,
@@ -1449,7 +1450,7 @@ static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx,
             dim3 grid((unsigned)sgeo.n_chunks, (unsigned)rows.n_rows);
             auto kernel = score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, false>;
             if constexpr (MODE == kModePaged) {
-                if (rows_share_keys(rows))
+                if (rows_share_keys(rows, gate))
                     kernel = score_stream_kernel<MODE, kScoreRing, 0, kWavesPerBlock, true>;
             }
             hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, (const uint16_t *)q_idx, w,
@@ -1505,8 +1506,8 @@ hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const 
     const ScoreGeom geo = score_geometry(rows.n_rows, ld, LSA_FP8_BLOCKS_PER_CU);
     dim3 grid((unsigned)geo.n_chunks, (unsigned)rows.n_rows);
     if (pages) {
-        auto kernel = rows_share_keys(rows) ? score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, true>
-                                            : score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, false>;
+        auto kernel = rows_share_keys(rows, RowGate{nullptr, 0}) ? score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, true>
+                                                                 : score_fp8_kernel<kModePaged, kFp8Ring, 0, 4, false>;
         hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, rows, q8, q_scale, w, k8, k_scale, k_sink, k_swa, pages,
                            M, P, scores, ld, ld, geo.chunk_elems, 0, nullptr, nullptr, (int64_t)0);
     } else

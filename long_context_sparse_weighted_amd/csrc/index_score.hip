@@ -1237,6 +1237,243 @@ __global__ __launch_bounds__(kGroupThreads, 1) void score_rows_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
+// Multi-row bf16 kernel over recalled pages (HI stage 2 of a prefill chunk, P = 128).  Each row of a
+// group scores only the M pages it recalled, but the rows of a chunk lie in one sequence and their page
+// sets overlap heavily, so the per-row kernel reads most pages once per recalling row.  Here a block
+// takes a range of kGpPages pages of the sequence and streams, two pages per stage as the flat
+// multi-row kernel streams 256 keys, only those pages of the range that some row of the group recalled
+// (each once per group); a wave (one row) scores the pages its own row recalled and skips the others,
+// so the matrix work is that of the recalled pages alone.  A page's 128 scores go to the row's slot of
+// that page: the output keeps the per-row kernel's layout (slot s, offset o at column s P + o), and
+// every column gets the same value as there (Eq. 10 inside mid(t), -inf elsewhere).
+//
+// Columns the stage loop does not produce -- slots whose page is -1, lies outside the sequence or
+// holds no token of the row's middle range, columns from M P to ld, every column of an empty row --
+// are written -inf by the blocks of the first page range.  A page listed at several slots of a row is
+// scored at one of them, and the wave then copies those scores to the others.
+constexpr int kGpPages = 256;  // pages per block
+constexpr int kGpP = 128;      // page size this kernel takes (a stage holds two pages)
+static_assert(2 * kGpP == kStageKeys && kGpPages % kWave == 0, "two pages per stage");
+
+__global__ __launch_bounds__(kGroupThreads, 1) void score_rows_paged_kernel(
+    RowsDev rows, const uint16_t *__restrict__ q_idx, const float *__restrict__ w, const uint16_t *__restrict__ keys,
+    int k_sink, int k_swa, const int32_t *__restrict__ pages, int M, float *__restrict__ scores, int64_t ld,
+    const uint8_t *row_mode, int want)
+{
+    const int chunk = blockIdx.x, grp = blockIdx.y;
+    if (!group_uniform(rows, row_mode, want, grp))
+        return;  // the per-row kernel scores these rows
+    __shared__ __attribute__((aligned(16))) uint16_t stage0[kStageElems];
+    __shared__ __attribute__((aligned(16))) uint16_t stage1[kStageElems];
+    __shared__ int32_t slot_of[kGroupRows][kGpPages];  // row's slot of page page0 + i (-1: not recalled)
+    __shared__ uint16_t upage[kGpPages];               // recalled pages of the range (from page0), ascending
+    __shared__ uint16_t umask[kGpPages];               // the rows that recalled upage[i]
+    __shared__ int32_t ucnt[kGpPages / kWave];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = lane_id();
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int r = grp * kGroupRows + wave;
+
+    const int32_t gseq = group_seq(rows, grp);  // every row that lies inside its sequence lies in this one
+    int64_t base = 0, L = 0;
+    if (gseq >= 0) {
+        base = rows.kv_off[gseq];
+        L = rows.kv_off[gseq + 1] - base;
+    }
+    const int64_t n_pages = (L + kGpP - 1) / kGpP;
+    const int64_t page0 = (int64_t)chunk * kGpPages;
+    const int64_t page_end = min(page0 + kGpPages, n_pages);
+
+    const RowInfo ri = row_info(rows, r);
+    const SiRanges si = si_ranges(ri, k_sink, k_swa);
+    const int64_t lo = si.mid_lo, hi = si.mid_hi < ri.L ? si.mid_hi : ri.L;  // the row's scored tokens
+    float *out = scores + (int64_t)r * ld;
+    const int32_t *prow = pages + (int64_t)r * M;
+    auto eligible = [&](int64_t pg) { return ri.valid && pg >= 0 && pg < n_pages && pg * kGpP < hi && (pg + 1) * kGpP > lo; };
+
+    if (chunk == 0) {
+        // -inf for the slots no page range produces, 64 slots at a time; then the columns past M P
+        for (int s0 = 0; s0 < M; s0 += kWave) {
+            const int s = s0 + lane;
+            const int64_t pg = prow[min(s, M - 1)];
+            // (pages past the grid's page ranges -- a sequence longer than the stated maximum -- too)
+            uint64_t todo = __ballot(s < M && !(eligible(pg) && pg < (int64_t)gridDim.x * kGpPages));
+            while (todo) {
+                const int b = __ffsll((long long)todo) - 1;
+                todo &= todo - 1;
+                out[(int64_t)(s0 + b) * kGpP + 2 * lane] = -INFINITY;
+                out[(int64_t)(s0 + b) * kGpP + 2 * lane + 1] = -INFINITY;
+            }
+        }
+        for (int64_t c = (int64_t)M * kGpP + lane; c < ld; c += kWave)
+            out[c] = -INFINITY;
+    }
+    if (page0 >= page_end)
+        return;  // (no barrier below is reached by any wave of the block)
+
+    for (int i = tid; i < kGroupRows * kGpPages; i += kGroupThreads)
+        (&slot_of[0][0])[i] = -1;
+    __syncthreads();
+    bool dup = false;  // this lane found a page at two slots of its row
+    for (int s0 = 0; s0 < M; s0 += kWave) {
+        const int s = s0 + lane;
+        const int64_t pg = s < M ? prow[s] : -1;
+        if (pg >= page0 && pg < page_end && eligible(pg))
+            dup |= atomicCAS(&slot_of[wave][pg - page0], -1, s) != -1;
+    }
+    __syncthreads();
+    // The recalled pages of the range in ascending order, with the rows that recalled each.
+    uint32_t my_mask = 0;
+    uint64_t my_ballot = 0;
+    if (wave < kGpPages / kWave) {
+        const int i = wave * kWave + lane;
+#pragma unroll
+        for (int rr = 0; rr < kGroupRows; ++rr)
+            my_mask |= (slot_of[rr][i] >= 0 ? 1u : 0u) << rr;
+        my_ballot = __ballot(my_mask != 0);
+        if (lane == 0)
+            ucnt[wave] = __popcll(my_ballot);
+    }
+    __syncthreads();
+    int total = 0, before = 0;
+#pragma unroll
+    for (int k = 0; k < kGpPages / kWave; ++k) {
+        before += k < wave ? ucnt[k] : 0;
+        total += ucnt[k];
+    }
+    if (wave < kGpPages / kWave && my_mask != 0) {
+        const int pos = before + (int)lanes_below(my_ballot);
+        upage[pos] = (uint16_t)(wave * kWave + lane);
+        umask[pos] = (uint16_t)my_mask;
+    }
+    __syncthreads();
+    total = __builtin_amdgcn_readfirstlane(total);
+    const int n_st = (total + 1) / 2;  // stages of two recalled pages (the last may hold one)
+
+    // A operands of the row, and the head weights of the 16 heads each lane ends up holding.
+    u32x4 qa[4][4];
+    float wv[4][4];
+    {
+        const uint16_t *qrow = q_idx + (int64_t)r * kHeads * kDim;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(qrow + (mt * 16 + n) * kDim + g * 8);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                qa[mt][ks] = src[4 * ks];
+            f32x4 v = *reinterpret_cast<const f32x4 *>(w + (int64_t)r * kHeads + mt * 16 + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                wv[mt][i] = v[i];
+        }
+    }
+    // DMA j = wave + 16 jj of a stage fills slots 64 j .. 64 j + 63, i.e. keys 4 j .. 4 j + 3 of the stage:
+    // this lane moves chunk c16 of stage key 4 wave + 64 jj + g, which lies in the stage's page jj / 2.
+    const int kk0 = 4 * wave + g;
+    const int c16 = n ^ (kk0 & 15);
+    const uint16_t *kseq = keys + base * kDim;
+    auto issue_stage = [&](int st, uint16_t *buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < kStageDma / kGroupWaves; ++jj) {
+            const int ui = min(2 * st + (jj >> 1), total - 1);  // (a stage of one page re-reads it)
+            const int64_t tok = min((page0 + upage[ui]) * kGpP + ((kk0 + 64 * jj) & (kGpP - 1)), L - 1);
+            __builtin_amdgcn_global_load_lds((glb_void *)(kseq + tok * kDim + c16 * 8),
+                                             (lds_void *)(buf + (wave + kGroupWaves * jj) * kWave * 8), 16, 0, 0);
+        }
+    };
+    auto score_tile = [&](const uint16_t *buf, int tt) __attribute__((always_inline)) -> float {
+        u32x4 b[4];
+        const uint16_t *krow = buf + (tt * kTile + n) * kDim;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            b[ks] = *reinterpret_cast<const u32x4 *>(krow + (((4 * ks + g) ^ n) * 8));
+        f32x4 acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 bb = __builtin_bit_cast(bf16x8, b[ks]);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[mt][ks]), bb, acc[mt],
+                                                                  0, 0, 0);
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v += wv[mt][i] * relu(acc[mt][i]);
+        return v;
+    };
+    // One stage: wait for its DMA, start the next stage's, then score the stage's pages this row recalled
+    // (four tiles at a time, folded as in the flat multi-row kernel: lane group g ends with tile t4 + g).
+    auto run_stage = [&](int st, const uint16_t *buf, uint16_t *next) __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA writes have landed
+        __syncthreads();                                  // ... and every other wave's
+        if (st + 1 < n_st)
+            issue_stage(st + 1, next);
+#pragma unroll 1
+        for (int t4 = 0; t4 < kStageTiles; t4 += 4) {
+            const int ui = 2 * st + t4 / 8;
+            if (ui >= total)
+                break;
+            if (!((__builtin_amdgcn_readfirstlane(umask[ui]) >> wave) & 1))
+                continue;  // (wave-uniform) the row did not recall this page
+            const int64_t pg = page0 + __builtin_amdgcn_readfirstlane(upage[ui]);
+            const int slot = __builtin_amdgcn_readfirstlane(slot_of[wave][pg - page0]);
+            float ya = 0.0f, yb = 0.0f;
+#pragma unroll 1
+            for (int h = 0; h < 2; ++h) {
+                int tt = t4 + 2 * h;
+                const float p0 = score_tile(buf, tt);
+                asm volatile("" : "+s"(tt) : "v"(p0));  // one tile in flight (registers)
+                const float p1 = score_tile(buf, tt + 1);
+                yb = sum_rows_swap16(p0, p1);
+                ya = h == 0 ? yb : ya;
+            }
+            const float v = sum_halves32(ya, yb);
+            const int off = ((t4 + g) & 7) * kTile + n;  // token pg P + off
+            const int64_t tok = pg * kGpP + off;
+            out[(int64_t)slot * kGpP + off] = tok >= lo && tok < hi ? v : -INFINITY;
+        }
+    };
+    if (n_st > 0)
+        issue_stage(0, stage0);
+    for (int st = 0; st < n_st; st += 2) {
+        run_stage(st, stage0, stage1);
+        if (st + 1 < n_st)
+            run_stage(st + 1, stage1, stage0);
+    }
+
+    // Pages listed at several slots of the row: copy the scored slot's columns to the others.
+    if (__ballot(dup) != 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's score stores are done
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // and are read back from L2
+        for (int s0 = 0; s0 < M; s0 += kWave) {
+            const int s = s0 + lane;
+            const int64_t pg = s < M ? prow[s] : -1;
+            int src = s;
+            if (pg >= page0 && pg < page_end && eligible(pg))
+                src = slot_of[wave][pg - page0];
+            uint64_t todo = __ballot(src != s);
+            while (todo) {
+                const int b = __ffsll((long long)todo) - 1;
+                todo &= todo - 1;
+                const int from = __shfl(src, b, kWave);
+                const float v0 = out[(int64_t)from * kGpP + 2 * lane], v1 = out[(int64_t)from * kGpP + 2 * lane + 1];
+                out[(int64_t)(s0 + b) * kGpP + 2 * lane] = v0;
+                out[(int64_t)(s0 + b) * kGpP + 2 * lane + 1] = v1;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // fp32 VALU kernel (any n_heads <= 64, head_dim in {64, 128}); one thread per column.
 
 template <int DI, int MODE>
@@ -1405,19 +1642,38 @@ static ScoreGeom score_geometry(int64_t n_rows, int64_t n_cols, int blocks_per_c
 }
 
 template <int MODE>
-static hipError_t launch_mode(int dtype, const RowsDev &rows, const void *q_idx, const float *w, const void *keys,
-                              int n_heads, int head_dim, int k_sink, int k_swa, const int64_t *sb_off,
-                              const int32_t *pages, int M, int P, int B, float *scores, int64_t ld, int64_t n_cols,
-                              RowGate gate, hipStream_t stream)
+static hipError_t launch_mode(int dtype, const RowsDev &rows, int64_t max_len, const void *q_idx, const float *w,
+                              const void *keys, int n_heads, int head_dim, int k_sink, int k_swa,
+                              const int64_t *sb_off, const int32_t *pages, int M, int P, int B, float *scores,
+                              int64_t ld, int64_t n_cols, RowGate gate, hipStream_t stream)
 {
     if (rows.n_rows == 0 || n_cols == 0)
         return hipSuccess;
     if (dtype == 1) {
         const ScoreGeom geo = score_geometry(rows.n_rows, n_cols);
-        const bool grouped = (MODE == kModeFlat || MODE == kModePageMean) && rows.n_rows >= kMinGroupedRows;
+        // (paged rows: the multi-row kernel over recalled pages takes pages of 128 tokens, prefill-like
+        // batches of at least a group's worth of rows per sequence -- decode batches keep their compact
+        // HI row lists -- and recall lists that cover at least a sixth of the sequence: sparser lists
+        // leave a group's waves mostly idle on each streamed page and the block bound by its DMA latency.
+        // Measured on 2048-row chunks: 4.9 / 6.3 / 8.5 ms at 256K / 512K / 1M tokens against 6.8 / 7.1 /
+        // 8.1 ms for the per-row kernel.)
+        const bool grouped =
+            (MODE == kModeFlat || MODE == kModePageMean ||
+             (MODE == kModePaged && P == kGpP && (int64_t)rows.n_rows >= (int64_t)kGroupRows * rows.n_seq &&
+              6 * (int64_t)M * P >= max_len)) &&
+            rows.n_rows >= kMinGroupedRows;
         // One sequence, whole groups, no gate: every group is uniform, so the per-row launch would only
         // find rows already scored (a prefill chunk: 73,728 blocks returning at once, 0.3 ms).
         const bool all_grouped = grouped && rows.n_seq == 1 && rows.n_rows % kGroupRows == 0 && !gate.row_mode;
+        if constexpr (MODE == kModePaged) {
+            if (grouped) {
+                const int64_t n_pages = (max(max_len, (int64_t)1) + kGpP - 1) / kGpP;
+                dim3 ggrid((unsigned)((n_pages + kGpPages - 1) / kGpPages), (unsigned)(rows.n_rows / kGroupRows));
+                hipLaunchKernelGGL(score_rows_paged_kernel, ggrid, dim3(kGroupThreads), 0, stream, rows,
+                                   (const uint16_t *)q_idx, w, (const uint16_t *)keys, k_sink, k_swa, pages, M, scores,
+                                   ld, gate.row_mode, gate.want);
+            }
+        }
         if constexpr (MODE == kModeFlat || MODE == kModePageMean) {
             if (grouped) {
                 dim3 ggrid((unsigned)geo.n_chunks, (unsigned)(rows.n_rows / kGroupRows));
@@ -1478,23 +1734,21 @@ hipError_t launch_index_score(int dtype, const RowsDev &rows, int64_t max_kv_len
                               const int32_t *pages, int M, int P, float *scores, int64_t ld, RowGate gate,
                               hipStream_t stream)
 {
-    (void)max_kv_len;
     if (pages)
-        return launch_mode<kModePaged>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, pages,
-                                       M, P, 1, scores, ld, ld, gate, stream);
-    return launch_mode<kModeFlat>(dtype, rows, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr, nullptr,
-                                  0, 1, 1, scores, ld, ld, gate, stream);
+        return launch_mode<kModePaged>(dtype, rows, max_kv_len, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa,
+                                       nullptr, pages, M, P, 1, scores, ld, ld, gate, stream);
+    return launch_mode<kModeFlat>(dtype, rows, max_kv_len, q_idx, w, k_idx, n_heads, head_dim, k_sink, k_swa, nullptr,
+                                  nullptr, 0, 1, 1, scores, ld, ld, gate, stream);
 }
 
 hipError_t launch_page_scores(int dtype, const RowsDev &rows, int64_t max_kv_len, const int64_t *sb_off,
                               const void *q_idx, const float *w, const void *k_mean, int n_heads, int head_dim,
                               int P, int B, float *page_scores, int64_t ld_ps, RowGate gate, hipStream_t stream)
 {
-    (void)max_kv_len;
     const int G = P / B;
     // Sub-block columns: ld_ps pages x G sub-blocks, so every page column is produced by one tile.
-    return launch_mode<kModePageMean>(dtype, rows, q_idx, w, k_mean, n_heads, head_dim, 0, 0, sb_off, nullptr, 0, P,
-                                      B, page_scores, ld_ps, ld_ps * G, gate, stream);
+    return launch_mode<kModePageMean>(dtype, rows, max_kv_len, q_idx, w, k_mean, n_heads, head_dim, 0, 0, sb_off,
+                                      nullptr, 0, P, B, page_scores, ld_ps, ld_ps * G, gate, stream);
 }
 
 hipError_t launch_index_score_fp8(const RowsDev &rows, const uint8_t *q8, const float *q_scale, const float *w,

@@ -143,6 +143,47 @@ def test_index_score_bf16_page_mapped(P):
     log("paged scores worst err/tol", assert_scores_close(host(g), want))
 
 
+@pytest.mark.parametrize("tail", [False, True])
+def test_index_score_bf16_page_mapped_grouped_rows(tail):
+    # Prefill-like batches (at least 16 rows per sequence) take the multi-row kernel over recalled pages:
+    # a group's recalled pages are streamed once and each row scores its own.  The lists overlap
+    # heavily (drawn from a small pool) and hold -1 padding, a page listed twice, pages past the
+    # sequence, the partial last page and pages straddling the end of mid(t); sequence 0 spans two
+    # page ranges of the kernel (266 pages).  Row 3 lies outside its sequence (t = L), and the rows
+    # of one group mix the two sequences, so the per-row kernel scores that group.  With a tail the
+    # batch is not whole groups (the last 8 rows go to the per-row kernel too).
+    rng = np.random.default_rng(5)
+    L0, L1 = 34000, 9000
+    t0 = sorted(rng.integers(26000, L0, 39).tolist())
+    t1 = sorted(rng.integers(3000, L1, 32 if tail else 40).tolist())
+    rows = [(0, t) for t in t0[:3]] + [(0, L0)] + [(0, t) for t in t0[3:]] + [(1, t) for t in t1]
+    x = custom_rows([L0, L1], rows, attn=False, seed=3)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    P, M = 128, 48  # (the multi-row kernel takes recall lists covering at least a sixth of the sequence)
+    n = len(rows)
+    pages = np.full((n, M), -1, np.int32)
+    for i, (sq, t) in enumerate(rows):
+        n_pages = -(-(L0 if sq == 0 else L1) // P)
+        pool = rng.choice(n_pages, 70, replace=False)
+        k = int(rng.integers(M - 6, M + 1))
+        pick = rng.choice(pool, k, replace=False)
+        pages[i, :k] = pick
+        if i % 5 == 0:
+            pages[i, M - 1] = pages[i, 0]        # listed twice
+        if i % 7 == 0:
+            pages[i, M - 2] = n_pages + 2        # past the sequence
+        if i % 3 == 0:
+            pages[i, 1] = n_pages - 1            # the partial last page
+            pages[i, 2] = (t - 1024) // P        # straddles the end of mid(t)
+    pg = torch.from_numpy(pages).to(DEV)
+    ld = M * P + 5
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), pages=pg, P=P, ld=ld)
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=ld, pages=pages, P=P)
+    log("grouped paged scores worst err/tol", assert_scores_close(host(g), want))
+
+
 # --------------------------------------------------------------------------------------------- a7 top-K
 
 
@@ -681,11 +722,12 @@ def test_layer_hi_vs_oracle(B):
     log(f"HI B={B}: needles picked {hits}/{sum(len(p) for p in x['needles'])}")
 
 
-def test_layer_hi_chunked_prefill_vs_oracle():
+@pytest.mark.parametrize("M", [24, 64])  # 64: recall lists long enough for the multi-row stage-2 kernel
+def test_layer_hi_chunked_prefill_vs_oracle(M):
     # HI on the rows of a prefill chunk with sub-blocks of 8: the page of row t also holds tokens after
     # t, which lie in the window or in the future and never yield candidates.  The oracle runs on rows
     # on both sides of the page edges crossed by the chunk (t = 38016 and 38144 start pages).
-    x = synth.prefill_chunk(38000, 160, device=DEV, seed=11, B=8, M=24, hi_min_len=0)
+    x = synth.prefill_chunk(38000, 160, device=DEV, seed=11, B=8, M=M, hi_min_len=0)
     c = x["cfg"]
     sb_off = lsa.sb_offsets(x["lengths"], c["B"])
     km = lsa.lsa_page_means(x["kv_off"], sb_off.to(DEV), x["k_idx"], c["B"], x["max_len"])

@@ -326,3 +326,47 @@ def test_ragged_mtp_full_size():
     o3, l3 = lsa.lsa_hybrid_attn(rows_of(x), x["q"], x["kv"], 512, c["scale"], (16, 1024, 1024), idx,
                                  idx_row=x["idx_row"])
     assert torch.equal(o3.view(torch.int16), out.view(torch.int16)) and torch.equal(l3, lse)
+
+
+# --------------------------------------------------------------------------------------------- HI prefill
+
+
+def test_hi_prefill_stage2_256k_full_size():
+    # HI stage 2 of the 2048-row prefill chunk at 256K as the benchmark times it (M = 1024 recalled pages
+    # of 128 tokens per row: the multi-row kernel over recalled pages).  The recall lists are seeded on
+    # the host, overlapping within each 16-row group as a chunk's lists do (1024 of a pool of 1536 of the
+    # row's middle pages); the oracle scores sampled rows on the same lists, then the token top-K of those
+    # rows is checked against the oracle's whole-row selection.
+    L, q_len, P, M, K = 262144, 2048, 128, 1024, 1024
+    x = synth.hi_prefill(L, device=DEV)
+    c = x["cfg"]
+    rows = lsa.RowsDesc(x["kv_off"], x["row_seq"], x["row_pos"], x["max_len"], L)
+    rng = np.random.default_rng(21)
+    pos = host(x["row_pos"]).astype(np.int64)
+    pages = np.empty((q_len, M), np.int32)
+    for g0 in range(0, q_len, 16):
+        last = (pos[g0] - c["k_swa"]) // P  # pages with middle tokens for every row of the group
+        pool = rng.choice(np.arange(0, last + 1), 1536, replace=False)
+        for r in range(g0, g0 + 16):
+            pages[r] = np.sort(rng.choice(pool, M, replace=False))  # (lsa_topk takes ascending lists)
+    pg = torch.from_numpy(pages).to(DEV)
+    bud = (c["k_sink"], c["k_swa"], K)
+    comp = lsa.lsa_index_score(rows, x["q_idx"], x["w"], x["k_idx"], bud, pages=pg, M=M, P=P)
+    idx = lsa.lsa_topk(comp, K, pages=pg, P=P)
+    torch.cuda.synchronize()
+    sample = [0, 777, 1500, 2047]
+    k_seq = seq_host(x, 0, "k_idx")
+    o = dict(kv_off=np.array([0, L], np.int64), row_seq=np.zeros(len(sample), np.int32),
+             row_pos=pos[sample].astype(np.int32), q_idx=host(x["q_idx"][sample]), w=host(x["w"][sample]))
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], k_seq, c["k_sink"],
+                           c["k_swa"], ld=M * P, pages=pages[sample], P=P)
+    got = host(comp)[sample]
+    log("HI stage-2 scores (sampled rows) worst err/tol", assert_scores_close(got, want))
+    w_idx = ref.topk(want, K, pages=pages[sample], P=P)
+    g_idx = host(idx)[sample]
+    for i in range(len(sample)):
+        th = kth_best(want[i], K)
+        slot = np.full(-(-L // P), -1, np.int64)
+        slot[pages[sample[i]]] = np.arange(M)
+        score_at = lambda d: want[i][slot[d // P] * P + d % P]  # oracle score of token position d
+        assert_idx_sets_match(g_idx[i:i + 1], w_idx[i:i + 1], lambda _, d: near_tie(score_at(np.asarray(d)), th))

@@ -184,6 +184,35 @@ def test_index_score_bf16_page_mapped_grouped_rows(tail):
     log("grouped paged scores worst err/tol", assert_scores_close(host(g), want))
 
 
+def test_index_score_bf16_page_mapped_grouped_short_rows():
+    # Four short sequences of 16 rows each (every group uniform): rows with an empty middle range
+    # (t < k_sink + k_swa), rows just past it, a row outside its sequence, M = 4 recalled pages of 128
+    # (lists of -1 only, pages past the sequence, the same page twice), ld = M P exactly.
+    rng = np.random.default_rng(8)
+    lengths = [1100, 2000, 2900, 3000]
+    rows = []
+    for b, L in enumerate(lengths):
+        ts = [0, 15, 16, 1039, 1040, 1041, L - 1, L] + sorted(rng.integers(1, L, 8).tolist())
+        rows += [(b, int(t)) for t in ts]
+    x = custom_rows(lengths, rows, attn=False, seed=6)
+    o = oracle_inputs(x)
+    c = x["cfg"]
+    P, M = 128, 4
+    pages = np.full((len(rows), M), -1, np.int32)
+    for i, (b, t) in enumerate(rows):
+        n_pages = -(-lengths[b] // P)
+        if i % 9 == 4:
+            continue  # an empty list
+        pages[i] = rng.choice(n_pages + 2, M, replace=False)
+        if i % 5 == 1:
+            pages[i, 3] = pages[i, 0]
+    pg = torch.from_numpy(pages).to(DEV)
+    g = lsa.lsa_index_score(rows_of(x), x["q_idx"], x["w"], x["k_idx"], budget_of(c), pages=pg, P=P, ld=M * P)
+    want = ref.index_score(o["kv_off"], o["row_seq"], o["row_pos"], o["q_idx"], o["w"], o["k_idx"], c["k_sink"],
+                           c["k_swa"], ld=M * P, pages=pages, P=P)
+    log("grouped paged scores, short rows: worst err/tol", assert_scores_close(host(g), want))
+
+
 # --------------------------------------------------------------------------------------------- a7 top-K
 
 

@@ -43,6 +43,28 @@ def time_on_stream(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps * 1e-3  # seconds per call
 
 
+SETTLE_S = 0.05
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Runs fn back to back for about `seconds` of GPU time before the warm-up steps.  After any idle
+    period the GPU's power management brings its clocks back over some tens of milliseconds: on the
+    1M decode step the first ~20 calls take 50-200 us longer than the later ones, then settle.  Returns
+    the number of calls run (reported with the result)."""
+    import torch
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    n = max(1, int(seconds / max(e0.elapsed_time(e1) * 1e-3, 1e-6)))
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    return n + 1
+
+
 def step_distribution(fn, reps, flush_bytes=0):
     """Per-call times (us) with one event pair around each call: p10 / median / p90. With flush_bytes > 0
     a scratch buffer of that size is written before every call (outside its events), so that the call starts
@@ -112,7 +134,9 @@ def run_length(L, batch, steps, warmup, seed=0):
     def step():
         layer(x["q"], x["kv"], idx, out, lse, q_idx=x["q_idx"], w=x["w"], k_idx=x["k_idx"])
 
-    # Whole-step timing: K steps between two synchronisations.
+    # Whole-step timing: K steps between two synchronisations, after the clocks have settled and the
+    # W warm-up steps.
+    n_settle = settle(step)
     torch.cuda.synchronize()
     for _ in range(warmup):
         step()
@@ -148,7 +172,7 @@ def run_length(L, batch, steps, warmup, seed=0):
     alg_bytes = k_bytes + attn_bytes + io_bytes
     flops = n * (mid * 64 * 128 * 2 + (c["k_sink"] + c["k_swa"] + c["k_sparse"]) * 128 * (576 + 512) * 2)
     del scores, sel, sel_ws
-    res = dict(L=L, batch=n, latency_us=t_step * 1e6, latency_us_events=t_step_ev * 1e6,
+    res = dict(L=L, batch=n, settle_calls=n_settle, latency_us=t_step * 1e6, latency_us_events=t_step_ev * 1e6,
                warm_us_p10=warm["p10"], warm_us_p50=warm["p50"], warm_us_p90=warm["p90"],
                cold_us_p10=cold["p10"], cold_us_p50=cold["p50"], cold_us_p90=cold["p90"],
                select_us=t_sel * 1e6, select_gbs=k_bytes / t_sel / 1e9, score_kernel_bytes=k_bytes,

@@ -54,6 +54,7 @@ def settle(fn, seconds=SETTLE_S):
     import torch
     s = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()  # (the first call also pays one-off costs: it does not size the loop)
     e0.record(s)
     fn()
     e1.record(s)
@@ -62,7 +63,7 @@ def settle(fn, seconds=SETTLE_S):
     for _ in range(n):
         fn()
     torch.cuda.synchronize()
-    return n + 1
+    return n + 2
 
 
 def step_distribution(fn, reps, flush_bytes=0):
